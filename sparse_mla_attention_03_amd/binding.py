@@ -1,0 +1,215 @@
+"""ctypes binding over libsparsemla (include/sparse_mla.h).
+
+Argument marshalling only: the functions below take torch tensors, check that
+their dtypes / devices / layouts are what the C ABI expects, allocate missing
+outputs and the workspace with torch, and call the library on torch's current
+HIP stream.  Every step of the computation runs in the library's kernels; if
+the library is not built this module raises instead of computing anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "csrc", "libsparsemla.so")
+
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
+DV = 512
+MAX_SPLITS = 64
+
+STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_DTYPE",
+                4: "SMLA_ERR_ALIGN", 5: "SMLA_ERR_INVALID_ARG", 6: "SMLA_ERR_UNSUPPORTED",
+                7: "SMLA_ERR_WORKSPACE", 8: "SMLA_ERR_HIP"}
+
+
+class SparseMLAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("kernel_events", ctypes.c_void_p * 2), ("reserved", ctypes.c_int32 * 4)]
+
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libsparsemla.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise SparseMLAError(8, f"{p} is not built; run `python -c 'import __graft_entry__ as g; "
+                                f"g.build()'` (hipcc, gfx950) first")
+    lib = ctypes.CDLL(p)
+    i64, i32, vp, f32, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    fwd_args = [vp, i64, i64, i64, i64, i64, vp, i32, i64, i64, vp, i64, i64, f32, f32, vp, vp,
+                vp, sz, vp]
+    lib.sparse_mla_fwd.argtypes = fwd_args
+    lib.sparse_mla_fwd.restype = ctypes.c_int
+    lib.sparse_mla_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(Options)]
+    lib.sparse_mla_fwd_ex.restype = ctypes.c_int
+    lib.sparse_mla_num_splits.argtypes = [i64, i64, i64, i64, i32, i32]
+    lib.sparse_mla_num_splits.restype = i32
+    lib.sparse_mla_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
+    lib.sparse_mla_workspace_bytes.restype = sz
+    lib.sparse_mla_quantize_q_fp8.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp]
+    lib.sparse_mla_quantize_q_fp8.restype = ctypes.c_int
+    lib.sparse_mla_status_string.argtypes = [ctypes.c_int]
+    lib.sparse_mla_status_string.restype = ctypes.c_char_p
+    lib.sparse_mla_last_error.argtypes = []
+    lib.sparse_mla_last_error.restype = ctypes.c_char_p
+    lib.sparse_mla_abi_version.argtypes = []
+    lib.sparse_mla_abi_version.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def sparse_mla_status_string(status: int) -> str:
+    return load_library().sparse_mla_status_string(int(status)).decode()
+
+
+def sparse_mla_last_error() -> str:
+    return load_library().sparse_mla_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise SparseMLAError(status, sparse_mla_last_error())
+
+
+def _kv_dtype(kv: torch.Tensor) -> int:
+    if kv.dtype == torch.bfloat16:
+        return KV_BF16
+    if kv.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return KV_FP8_E4M3
+    raise TypeError(f"kv_pool must be bfloat16 or e4m3 (uint8 / float8_e4m3fn), got {kv.dtype}")
+
+
+def _stream_handle(dev: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def sparse_mla_num_splits(T: int, H: int, K: int, Dqk: int, kv_dtype: int, num_splits: int = 0) -> int:
+    s = int(load_library().sparse_mla_num_splits(T, H, K, Dqk, kv_dtype, num_splits))
+    if s <= 0:
+        raise SparseMLAError(5, sparse_mla_last_error())
+    return s
+
+
+def sparse_mla_workspace_bytes(T: int, H: int, K: int, Dqk: int, kv_dtype: int,
+                               num_splits: int = 0) -> int:
+    n = load_library().sparse_mla_workspace_bytes(T, H, K, Dqk, kv_dtype, num_splits)
+    if n == ctypes.c_size_t(-1).value:
+        raise SparseMLAError(5, sparse_mla_last_error())
+    return int(n)
+
+
+def _pool_shape(kv_pool: torch.Tensor):
+    if kv_pool.dim() == 3:
+        nb, bs, D = kv_pool.shape
+    elif kv_pool.dim() == 2:
+        (nb, D), bs = kv_pool.shape, 1
+    else:
+        raise ValueError("kv_pool must be [num_blocks, block_size, Dqk] or [N, Dqk]")
+    return nb, bs, D
+
+
+def sparse_mla_fwd_ex(q: torch.Tensor, kv_pool: torch.Tensor, topk_idx: torch.Tensor,
+                      sm_scale: float, kv_scale: float = 1.0, out: torch.Tensor | None = None,
+                      lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      num_splits: int = 0, stream=None, kernel_events=None):
+    """Sparse MLA forward; returns (out bf16 [T,H,512], lse fp32 [T,H]).
+
+    kernel_events: optional pair of raw hipEvent_t handles (ints) the library
+    records around its main kernel (instrumentation for benchmarks)."""
+    lib = load_library()
+    if q.dim() != 3 or q.dtype != torch.bfloat16:
+        raise TypeError("q must be bfloat16 [T, H, Dqk]")
+    if not q.is_cuda:
+        raise ValueError("q must live on a GPU")
+    T, H, D = q.shape
+    if T > 0 and q.stride(2) != 1:
+        raise ValueError("q's last dimension must be contiguous")
+    nb, bs, Dkv = _pool_shape(kv_pool)
+    if Dkv != D:
+        raise ValueError(f"kv_pool rows are {Dkv} wide, q rows {D}")
+    if not kv_pool.is_contiguous():
+        raise ValueError("kv_pool must be contiguous")
+    kvd = _kv_dtype(kv_pool)
+    if topk_idx.dim() != 2 or topk_idx.dtype != torch.int32 or topk_idx.shape[0] != T:
+        raise TypeError("topk_idx must be int32 [T, K]")
+    K = topk_idx.shape[1]
+    if T > 0 and K > 1 and topk_idx.stride(1) != 1:
+        raise ValueError("topk_idx rows must be contiguous")
+    for t_, name in ((kv_pool, "kv_pool"), (topk_idx, "topk_idx")):
+        if t_.device != q.device:
+            raise ValueError(f"{name} is on {t_.device}, q on {q.device}")
+    if out is None:
+        out = torch.empty((T, H, DV), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if out.shape != (T, H, DV) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [T, H, 512] tensor")
+    if lse.shape != (T, H) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [T, H] tensor")
+    ws_ptr, ws_bytes = None, 0
+    if T > 0:
+        need = sparse_mla_workspace_bytes(T, H, K, D, kvd, num_splits)
+        if need > 0:
+            if workspace is None or workspace.numel() * workspace.element_size() < need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            ws_ptr = workspace.data_ptr()
+            ws_bytes = workspace.numel() * workspace.element_size()
+    opts = Options()
+    opts.num_splits = num_splits
+    if kernel_events is not None:
+        opts.kernel_events[0], opts.kernel_events[1] = kernel_events
+    st = lib.sparse_mla_fwd_ex(
+        q.data_ptr(), T, H, D, q.stride(0) if T else 0, q.stride(1) if T else 0,
+        kv_pool.data_ptr(), kvd, nb, bs,
+        topk_idx.data_ptr() if topk_idx.numel() else None, K, topk_idx.stride(0) if T else 0,
+        float(sm_scale), float(kv_scale), out.data_ptr(), lse.data_ptr(),
+        ws_ptr, ws_bytes, _stream_handle(q.device, stream), ctypes.byref(opts))
+    _check(st)
+    return out, lse
+
+
+def sparse_mla_fwd(q, kv_pool, topk_idx, sm_scale, kv_scale=1.0, out=None, lse=None,
+                   workspace=None, stream=None):
+    """Sparse MLA forward with the library's automatic split-K choice."""
+    return sparse_mla_fwd_ex(q, kv_pool, topk_idx, sm_scale, kv_scale, out=out, lse=lse,
+                             workspace=workspace, num_splits=0, stream=stream)
+
+
+def sparse_mla_quantize_q_fp8(q: torch.Tensor, codes: torch.Tensor | None = None,
+                              scales: torch.Tensor | None = None, stream=None):
+    """Per-tile e4m3 quantisation of q on the GPU -> (codes uint8 [T,H,Dqk], scales fp32 [T,G])."""
+    lib = load_library()
+    if q.dim() != 3 or q.dtype != torch.bfloat16 or not q.is_cuda:
+        raise TypeError("q must be a GPU bfloat16 [T, H, Dqk] tensor")
+    T, H, D = q.shape
+    if T > 0 and q.stride(2) != 1:
+        raise ValueError("q's last dimension must be contiguous")
+    G = (H + 63) // 64
+    if codes is None:
+        codes = torch.empty((T, H, D), dtype=torch.uint8, device=q.device)
+    if scales is None:
+        scales = torch.empty((T, G), dtype=torch.float32, device=q.device)
+    st = lib.sparse_mla_quantize_q_fp8(q.data_ptr(), T, H, D, q.stride(0) if T else 0,
+                                       q.stride(1) if T else 0, codes.data_ptr(),
+                                       scales.data_ptr(), _stream_handle(q.device, stream))
+    _check(st)
+    return codes, scales
