@@ -1,0 +1,277 @@
+"""Benchmark of the sparse MLA forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the library (gather + QK^T + softmax + PV, plus the
+split-K combine when the call splits) on one batch of synthetic input that is
+already resident in HBM.  The default workload is the GLM-5.3-Flash-like bf16
+decode: 32 sequences x 1 query token, 16 heads, 512-wide rope-free rows, top-k
+2048 out of 131072-token paged contexts (block size 64).  Eight independent
+index sets (and q) rotate from step to step so the 512 MiB they touch does
+not fit the 256 MB Infinity Cache.
+
+Prints ONE JSON line: value = gathered KV bytes / second (whole job), plus
+`roofline` for the main kernel (algorithmic gathered bytes / its own average
+duration, timed with HIP events the library records around it on the same
+stream) and `cpu_baseline` (the fp64 oracle on the host, same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
+INDEX_SETS = 8
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t pairs via the HIP runtime (the library records them on its stream)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev.append(e.value)
+
+    def pair(self, i):
+        return self.ev[2 * i], self.ev[2 * i + 1]
+
+    def elapsed_ms(self, i) -> float:
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[2 * i], self.ev[2 * i + 1]) == 0
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_mla_attention_03_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, launches_bytes: float):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cases, budget_s: float):
+    """The fp64 oracle (as it stands) on the host: whole decode calls of the same
+    workload, repeated over index sets until about `budget_s` seconds."""
+    import numpy as np
+    import oracle
+    from tests.helpers import bits16, codes8
+
+    done_bytes, t_total, n_calls, n_tok = 0, 0.0, 0, 0
+    # stage host copies first (not timed): the rows each call gathers, remapped
+    staged = []
+    for case in cases:
+        idx = case.topk_idx.cpu().numpy()
+        N = case.kv_pool.shape[0] * case.kv_pool.shape[1]
+        valid = (idx >= 0) & (idx < N)
+        rows = np.unique(idx[valid]).astype(np.int64)
+        remap = np.full(idx.shape, -1, np.int32)
+        remap[valid] = np.searchsorted(rows, idx[valid])
+        import torch
+        flat = case.kv_pool.reshape(-1, case.kv_pool.shape[-1])
+        sub = flat[torch.from_numpy(rows).to(flat.device)].cpu()
+        kv = bits16(sub) if sub.dtype == torch.bfloat16 else codes8(sub)
+        staged.append((bits16(case.q.cpu()), np.ascontiguousarray(kv), remap,
+                       int(valid.sum()) * case.spec.Dqk * (2 if case.spec.kv_dtype == "bf16" else 1),
+                       case))
+        if len(staged) >= 2:
+            break
+    while t_total < budget_s and n_calls < 8:
+        q, kv, remap, nbytes, case = staged[n_calls % len(staged)]
+        t0 = time.perf_counter()
+        oracle.sparse_mla_fwd(q, kv, remap, case.sm_scale, case.kv_scale)
+        t_total += time.perf_counter() - t0
+        done_bytes += nbytes
+        n_calls += 1
+        n_tok += q.shape[0]
+    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n_calls} whole calls of the same workload ({n_tok} query tokens, "
+                      f"fp64 C oracle, OpenMP over (token, head)), {t_total:.1f} s",
+            "us_per_call": round(t_total / n_calls * 1e6, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the sparse MLA "
+              f"forward pass here runs on a single MI355X with no sharding or collectives.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_03_amd import synth
+    from sparse_mla_attention_03_amd.binding import (load_library, sparse_mla_fwd_ex,
+                                                     sparse_mla_num_splits,
+                                                     sparse_mla_workspace_bytes)
+
+    load_library()
+    dev = torch.device("cuda:0")
+    spec = synth.CONFIGS[args.workload]
+    cases = synth.make_case(spec, device="cuda:0", index_sets=INDEX_SETS)
+    kvd = 0 if spec.kv_dtype == "bf16" else 1
+    elem = 2 if spec.kv_dtype == "bf16" else 1
+    S = sparse_mla_num_splits(spec.T, spec.H, spec.K, spec.Dqk, kvd, 0)
+    ws_bytes = sparse_mla_workspace_bytes(spec.T, spec.H, spec.K, spec.Dqk, kvd, 0)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((spec.T, spec.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((spec.T, spec.H), dtype=torch.float32, device=dev)
+
+    valid_rows = []
+    for c in cases:
+        idx = c.topk_idx
+        valid_rows.append(int(((idx >= 0) & (idx < spec.N)).sum().item()))
+    gathered = [v * spec.Dqk * elem for v in valid_rows]            # algorithmic bytes per call
+    flops = [v * 2 * spec.H * (spec.Dqk + 512) for v in valid_rows]  # algorithmic FLOP per call
+
+    def call(i, events=None):
+        c = cases[i % INDEX_SETS]
+        sparse_mla_fwd_ex(c.q, c.kv_pool, c.topk_idx, c.sm_scale, c.kv_scale, out=out, lse=lse,
+                          workspace=ws, num_splits=0, kernel_events=events)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+
+    # ---- whole-job timing: the K calls captured once as a HIP graph (no host
+    # launch overhead inside the timed region), replayed back to back
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for i in range(args.steps):
+            call(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    # a replay must reproduce the eager result of its last call bit for bit
+    g_out, g_lse = out.clone(), lse.clone()
+    call(args.steps - 1)
+    torch.cuda.synchronize()
+    if not (torch.equal(g_out.view(torch.int16), out.view(torch.int16)) and torch.equal(g_lse, lse)):
+        raise RuntimeError("graph replay differs from the eager call")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t0.elapsed_time(t1)
+    ms_per_step = ms_total / args.steps
+    bytes_total = sum(gathered[i % INDEX_SETS] for i in range(args.steps))
+    flop_total = sum(flops[i % INDEX_SETS] for i in range(args.steps))
+    decode = spec.mode != "prefill"
+    if decode:
+        value, unit = bytes_total / (ms_total * 1e-3) / 1e9, "GB/s"
+    else:
+        value, unit = flop_total / (ms_total * 1e-3) / 1e12, "TFLOP/s"
+    del graph
+
+    # ---- main-kernel timing: HIP events the library records around that kernel
+    ev = HipEvents(args.steps)
+    for i in range(args.steps):
+        call(i, events=ev.pair(i))
+    torch.cuda.synchronize()
+    kern_ms = [ev.elapsed_ms(i) for i in range(args.steps)]
+    ev.close()
+    kern_avg_ms = float(np.mean(kern_ms))
+    avg_bytes = bytes_total / args.steps
+    avg_flop = flop_total / args.steps
+    achieved = avg_bytes / (kern_avg_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(args.workload, avg_bytes)
+
+    if decode:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        tflops = avg_flop / (kern_avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                    "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cases, args.cpu_seconds)
+
+    line = {
+        "metric": "sparse-MLA decode \u00b5s/call + gathered-KV HBM GB/s; prefill TFLOP/s (1 MI355X)",
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_call": round(ms_per_step * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "tokens": spec.T, "heads": spec.H, "dqk": spec.Dqk,
+                   "dv": 512, "topk": spec.K, "context": spec.ctx, "block_size": spec.block_size,
+                   "kv": spec.kv_dtype, "splits": S, "index_sets": INDEX_SETS,
+                   "gathered_bytes_per_call": int(avg_bytes),
+                   "tflops": round(avg_flop / (ms_per_step * 1e-3) / 1e12, 3)},
+        "roofline": roofline,
+        "main_kernel_us": round(kern_avg_ms * 1e3, 3),
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

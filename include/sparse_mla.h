@@ -1,0 +1,163 @@
+/*
+ * sparse_mla.h -- C ABI of libsparsemla, the sparse MLA attention forward pass
+ * on AMD MI355X (gfx950).
+ *
+ * The operation (vLLM PR "[ROCm][Perf][GLM-5.3-Flash] Enable AITER sparse MLA
+ * on gfx942, including FP8 KV", Overview and Details; vLLM PR "[ROCm][DSv4.1]
+ * [Perf] Route gfx942 sparse MLA prefill to AITER pa_prefill_sparse", What
+ * changed: one shared KV pool; vLLM PR "[ROCm][MLA][Perf] Fuse decode QK-RoPE
+ * + Q-concat + KV-concat + KV-cache write for sparse MLA", Test plan: a cache
+ * row is concat(kv_c, RoPE(k_pe)), so V is its first 512 columns):
+ *
+ *   every query token t has H heads (MQA style: all heads share one latent KV
+ *   pool).  Token t attends only to the rows named by its top-k list
+ *   topk_idx[t, 0..K-1]; a row is Dqk wide (512 rope-free, or 512 + 64 with
+ *   RoPE) and V is its first 512 columns.  For each (t, h):
+ *     s_j = sm_scale * <qhat[t,h,:], kv_scale * row_j[0:Dqk]>
+ *     lse = ln sum_j exp(s_j)
+ *     out = sum_j exp(s_j - lse) * kv_scale * row_j[0:512]
+ *   Entries outside [0, N) (N = num_blocks * block_size), e.g. -1 padding,
+ *   are never read and contribute nothing; duplicates count once per
+ *   occurrence.  A token with no valid entry gets out = +0 and lse = -inf.
+ *
+ *   qhat = q for bf16 KV.  For OCP fp8-e4m3 KV the QK dots run in fp8: q is
+ *   quantised inside the kernel per tile (the first page, Details: "the
+ *   kernel quantizes q per tile"), a tile being heads [64g, min(64g+64, H))
+ *   of one token over all Dqk columns:  s_q = amax|q| / 448 (fp32; 1 if the
+ *   tile is all zero), code = e4m3_rne(q / s_q) (fp32 division), qhat =
+ *   s_q * code.  PV runs in bf16 on exactly dequantised V.
+ *
+ * Memory: every tensor pointer is a DEVICE pointer owned by the caller; the
+ * library allocates nothing and keeps no device memory.  Calls are
+ * asynchronous on the given stream; results are valid once the stream reaches
+ * them.  On any error status nothing is launched and out/lse are untouched.
+ */
+#ifndef SPARSE_MLA_H
+#define SPARSE_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMLA_ABI_VERSION 1
+#define SMLA_DV 512          /* width of V and of out */
+#define SMLA_MAX_SPLITS 64   /* upper bound on the split-K factor */
+
+typedef enum {
+  SMLA_OK = 0,
+  SMLA_ERR_NULL = 1,         /* a required pointer is NULL */
+  SMLA_ERR_SHAPE = 2,        /* negative or out-of-range size or stride */
+  SMLA_ERR_DTYPE = 3,        /* unknown kv dtype */
+  SMLA_ERR_ALIGN = 4,        /* pointer or stride breaks the 16-byte rule */
+  SMLA_ERR_INVALID_ARG = 5,  /* non-finite scale, bad option value */
+  SMLA_ERR_UNSUPPORTED = 6,  /* well formed but not implemented (reason in last_error) */
+  SMLA_ERR_WORKSPACE = 7,    /* workspace missing or too small */
+  SMLA_ERR_HIP = 8           /* HIP runtime error (device query or launch) */
+} smla_status_t;
+
+typedef enum {
+  SMLA_KV_BF16 = 0,          /* kv_pool holds bf16 */
+  SMLA_KV_FP8_E4M3 = 1       /* kv_pool holds OCP e4m3 ("e4m3fn") codes */
+} smla_kv_dtype_t;
+
+typedef struct {
+  int32_t num_splits;        /* split-K factor over each top-k list; 0 = automatic,
+                                otherwise 1..SMLA_MAX_SPLITS */
+  int32_t reserved0;         /* must be zero */
+  void* kernel_events[2];    /* optional instrumentation: two caller-created hipEvent_t
+                                recorded on the stream immediately before and after the
+                                main (gather + attention) kernel, not around the split
+                                combine; NULL = not recorded */
+  int32_t reserved[4];       /* must be zero */
+} smla_options_t;
+
+/*
+ * sparse_mla_fwd -- the forward pass.
+ *
+ *   q            bf16 [T, H, Dqk]; element (t,h,d) at q[t*q_stride_t + h*q_stride_h + d].
+ *                Strides are in elements, last dimension contiguous.  q, q_stride_t
+ *                and q_stride_h must keep every row 16-byte aligned (pointer
+ *                16-byte aligned, strides multiples of 8).  Strided (non-packed)
+ *                q is computed correctly, never assumed packed.
+ *   T, H, Dqk    tokens, heads (multiple of 16), row width (512 or 576).
+ *   kv_pool      [num_blocks, block_size, Dqk] packed rows of kv_dtype, 16-byte
+ *                aligned.  Viewed as N = num_blocks*block_size flat slots.
+ *   topk_idx     int32 [T, K]; entry (t,k) at topk_idx[t*idx_stride_t + k]; each
+ *                entry is a flat slot id in [0, N); anything else is padding.
+ *   sm_scale     softmax scale (finite), e.g. 1/sqrt(Dqk).
+ *   kv_scale     dequantisation multiplier applied to K and V (finite); 1.0 for
+ *                bf16 pools, the per-tensor scale for fp8 pools.
+ *   out          bf16 [T, H, 512], packed, 16-byte aligned (written).
+ *   lse          fp32 [T, H], packed (written), natural log.
+ *   workspace    device scratch of at least sparse_mla_workspace_bytes(...) bytes,
+ *                16-byte aligned; may be NULL when that size is 0.  Its contents
+ *                need no initialisation and are garbage afterwards.  Two calls
+ *                that run concurrently must not share a workspace.
+ *   stream       hipStream_t to launch on (NULL = default stream).
+ *
+ * T == 0 is a no-op.  K == 0 makes every token all-padding.
+ */
+smla_status_t sparse_mla_fwd(const void* q, int64_t T, int64_t H, int64_t Dqk,
+                             int64_t q_stride_t, int64_t q_stride_h,
+                             const void* kv_pool, int32_t kv_dtype,
+                             int64_t num_blocks, int64_t block_size,
+                             const int32_t* topk_idx, int64_t K, int64_t idx_stride_t,
+                             float sm_scale, float kv_scale,
+                             void* out, float* lse,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Same as sparse_mla_fwd, with options (opts may be NULL = all defaults). */
+smla_status_t sparse_mla_fwd_ex(const void* q, int64_t T, int64_t H, int64_t Dqk,
+                                int64_t q_stride_t, int64_t q_stride_h,
+                                const void* kv_pool, int32_t kv_dtype,
+                                int64_t num_blocks, int64_t block_size,
+                                const int32_t* topk_idx, int64_t K, int64_t idx_stride_t,
+                                float sm_scale, float kv_scale,
+                                void* out, float* lse,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream, const smla_options_t* opts);
+
+/*
+ * Split-K factor the library picks for this shape on the current device
+ * (queries its compute-unit count).  num_splits > 0 is validated and returned
+ * as is.  Returns 0 on error (see sparse_mla_last_error).
+ */
+int32_t sparse_mla_num_splits(int64_t T, int64_t H, int64_t K, int64_t Dqk,
+                              int32_t kv_dtype, int32_t num_splits);
+
+/*
+ * Workspace bytes a call with these sizes needs (num_splits as in
+ * smla_options_t; 0 = automatic, which queries the current device).
+ * Returns (size_t)-1 on error.
+ */
+size_t sparse_mla_workspace_bytes(int64_t T, int64_t H, int64_t K, int64_t Dqk,
+                                  int32_t kv_dtype, int32_t num_splits);
+
+/*
+ * The fp8 per-tile q quantisation step on its own (the same device code the
+ * fp8 forward pass runs before its QK dots), for checking it bit by bit.
+ *   q       bf16 [T, H, Dqk] with strides as in sparse_mla_fwd.
+ *   codes   uint8 [T, H, Dqk] packed (written): OCP e4m3 codes of q / s_q.
+ *   scales  fp32 [T, ceil(H/64)] packed (written): s_q per (token, tile).
+ */
+smla_status_t sparse_mla_quantize_q_fp8(const void* q, int64_t T, int64_t H, int64_t Dqk,
+                                        int64_t q_stride_t, int64_t q_stride_h,
+                                        uint8_t* codes, float* scales, void* stream);
+
+/* Static description of a status code. */
+const char* sparse_mla_status_string(smla_status_t status);
+
+/* Detail of the last error returned on this thread ("" if none). */
+const char* sparse_mla_last_error(void);
+
+/* SMLA_ABI_VERSION of the built library. */
+int32_t sparse_mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSE_MLA_H */

@@ -1,0 +1,68 @@
+"""Build libsparsemla.so for gfx950 with hipcc (in-tree, next to this file).
+
+    python -m sparse_mla_attention_03_amd.csrc.build      # or build.build()
+
+The two translation units compile in parallel, then link into one shared
+library exporting the C ABI of include/sparse_mla.h.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libsparsemla.so")
+SOURCES = ["smla_api.hip", "smla_kernels.hip"]
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # keep the compiler from forming packed fp32 (v_pk_*_f32) instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", INCLUDE, "-I", HERE,
+]
+
+
+def _hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cand = os.path.join(rocm, "bin", "hipcc")
+    return cand if os.path.exists(cand) else "hipcc"
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = _hipcc()
+    objs = []
+
+    def compile_one(src: str) -> str:
+        obj = os.path.join(HERE, "_build", src.replace(".hip", ".o"))
+        os.makedirs(os.path.dirname(obj), exist_ok=True)
+        cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(HERE, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                         if "packed-fp32-ops" not in l)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{msgs}")
+        if verbose and msgs.strip():
+            print(msgs)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

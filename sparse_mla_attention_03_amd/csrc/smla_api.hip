@@ -1,0 +1,280 @@
+// smla_api.hip -- the C ABI of libsparsemla: argument validation, split-K
+// planning, workspace carving and kernel launches (include/sparse_mla.h).
+//
+// Every check runs on the host before anything is launched; a failed check
+// returns a status, records a reason for sparse_mla_last_error() and leaves
+// out/lse untouched.  The library allocates no device memory.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "sparse_mla.h"
+#include "smla_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+smla_status_t fail(smla_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+smla_status_t fail(smla_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Compute units of the current device, cached per device id (read-only after
+// the first query; benign races write the same value).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+smla_status_t device_cu_count(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices) {
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) { *cus = c; return SMLA_OK; }
+  }
+  int c = 0;
+  e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || c <= 0)
+    return fail(SMLA_ERR_HIP, "hipDeviceGetAttribute(CU count): %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return SMLA_OK;
+}
+
+struct Plan {
+  int32_t S = 1;        // split-K factor
+  int32_t rps = 0;      // top-k entries per split (multiple of kBK)
+  size_t ws_bytes = 0;  // workspace: S*T*H*512 fp32 partials + S*T*H fp32 lse
+};
+
+smla_status_t check_sizes(int64_t T, int64_t H, int64_t K, int64_t Dqk, int32_t kv_dtype) {
+  if (T < 0 || H <= 0 || K < 0 || Dqk <= 0)
+    return fail(SMLA_ERR_SHAPE, "bad sizes T=%lld H=%lld K=%lld Dqk=%lld", (long long)T,
+                (long long)H, (long long)K, (long long)Dqk);
+  if (kv_dtype != SMLA_KV_BF16 && kv_dtype != SMLA_KV_FP8_E4M3)
+    return fail(SMLA_ERR_DTYPE, "unknown kv dtype %d", kv_dtype);
+  if (H % 16 != 0)
+    return fail(SMLA_ERR_UNSUPPORTED, "H=%lld unsupported: heads must be a multiple of 16", (long long)H);
+  if (Dqk != 512 && Dqk != 576)
+    return fail(SMLA_ERR_UNSUPPORTED, "Dqk=%lld unsupported: rows must be 512 or 576 wide", (long long)Dqk);
+  if (T > (1 << 24) || H > 4096 || K > (1 << 24))
+    return fail(SMLA_ERR_SHAPE, "sizes out of range T=%lld H=%lld K=%lld", (long long)T,
+                (long long)H, (long long)K);
+  return SMLA_OK;
+}
+
+// Split-K choice: enough (token, head group, split) units to give every
+// compute unit one workgroup, never more splits than 64-entry tiles.
+smla_status_t make_plan(int64_t T, int64_t H, int64_t K, int32_t req, Plan* plan) {
+  const int64_t tiles = (K + smla::kBK - 1) / smla::kBK;
+  const int64_t HG = H / smla::heads_per_workgroup(H);
+  int64_t S = 1;
+  if (req < 0 || req > SMLA_MAX_SPLITS)
+    return fail(SMLA_ERR_INVALID_ARG, "num_splits=%d outside 0..%d", req, SMLA_MAX_SPLITS);
+  if (req > 0) {
+    S = req;
+  } else if (T > 0 && tiles > 1) {
+    int cus = 0;
+    smla_status_t st = device_cu_count(&cus);
+    if (st != SMLA_OK) return st;
+    const int64_t units = T * HG;
+    if (units < cus) S = (cus + units - 1) / units;
+  }
+  if (S > tiles) S = tiles > 0 ? tiles : 1;
+  if (S > SMLA_MAX_SPLITS) S = SMLA_MAX_SPLITS;
+  const int64_t tps = tiles > 0 ? (tiles + S - 1) / S : 1;   // tiles per split
+  if (tiles > 0) S = (tiles + tps - 1) / tps;                 // drop empty splits
+  plan->S = (int32_t)S;
+  plan->rps = (int32_t)(tps * smla::kBK);
+  plan->ws_bytes = S > 1 ? (size_t)S * T * H * (smla::kDV + 1) * sizeof(float) : 0;
+  return SMLA_OK;
+}
+
+smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t q_stride_t,
+                       int64_t q_stride_h, const void* kv_pool, int32_t kv_dtype, int64_t num_blocks,
+                       int64_t block_size, const int32_t* topk_idx, int64_t K, int64_t idx_stride_t,
+                       float sm_scale, float kv_scale, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream, const smla_options_t* opts) {
+  g_last_error.clear();
+  smla_status_t st = check_sizes(T, H, K, Dqk, kv_dtype);
+  if (st != SMLA_OK) return st;
+  if (num_blocks < 0 || block_size <= 0)
+    return fail(SMLA_ERR_SHAPE, "bad pool shape num_blocks=%lld block_size=%lld",
+                (long long)num_blocks, (long long)block_size);
+  if (q_stride_t < 0 || q_stride_h < 0 || idx_stride_t < 0)
+    return fail(SMLA_ERR_SHAPE, "negative stride");
+  if (!std::isfinite(sm_scale) || !std::isfinite(kv_scale))
+    return fail(SMLA_ERR_INVALID_ARG, "sm_scale and kv_scale must be finite");
+  int32_t req = 0;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (opts) {
+    if (opts->reserved0 != 0) return fail(SMLA_ERR_INVALID_ARG, "options.reserved0 must be 0");
+    for (int i = 0; i < 4; ++i)
+      if (opts->reserved[i] != 0) return fail(SMLA_ERR_INVALID_ARG, "options.reserved[%d] must be 0", i);
+    req = opts->num_splits;
+    ev0 = static_cast<hipEvent_t>(opts->kernel_events[0]);
+    ev1 = static_cast<hipEvent_t>(opts->kernel_events[1]);
+    if ((ev0 == nullptr) != (ev1 == nullptr))
+      return fail(SMLA_ERR_INVALID_ARG, "options.kernel_events: give both events or neither");
+  }
+  if (req < 0 || req > SMLA_MAX_SPLITS)
+    return fail(SMLA_ERR_INVALID_ARG, "num_splits=%d outside 0..%d", req, SMLA_MAX_SPLITS);
+  if (T == 0) return SMLA_OK;
+  if (!q || !kv_pool || !out || !lse || (K > 0 && !topk_idx))
+    return fail(SMLA_ERR_NULL, "null tensor pointer (q, kv_pool, topk_idx, out and lse are required)");
+  if (!aligned(q, 16) || q_stride_t % 8 || q_stride_h % 8)
+    return fail(SMLA_ERR_ALIGN, "q must be 16-byte aligned with strides that are multiples of 8 elements");
+  if (!aligned(kv_pool, 16)) return fail(SMLA_ERR_ALIGN, "kv_pool must be 16-byte aligned");
+  if (!aligned(out, 16)) return fail(SMLA_ERR_ALIGN, "out must be 16-byte aligned");
+  if (!aligned(lse, 4) || (topk_idx && !aligned(topk_idx, 4)))
+    return fail(SMLA_ERR_ALIGN, "lse and topk_idx must be 4-byte aligned");
+
+  Plan plan;
+  st = make_plan(T, H, K, req, &plan);
+  if (st != SMLA_OK) return st;
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes)
+      return fail(SMLA_ERR_WORKSPACE, "workspace of %zu bytes needed for %d splits, got %zu",
+                  plan.ws_bytes, plan.S, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(SMLA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+
+  smla::FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_st = q_stride_t;
+  p.q_sh = q_stride_h;
+  p.kv = static_cast<const uint8_t*>(kv_pool);
+  p.N = num_blocks * block_size;
+  p.idx = topk_idx;
+  p.idx_st = idx_stride_t;
+  p.T = (int32_t)T;
+  p.H = (int32_t)H;
+  p.K = (int32_t)K;
+  p.S = plan.S;
+  p.rps = plan.rps;
+  p.sm_scale = sm_scale;
+  p.kv_scale = kv_scale;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  if (plan.S > 1) {
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = p.part_o + (size_t)plan.S * T * H * smla::kDV;
+  }
+  if (getenv("SPARSEMLA_LOG"))
+    fprintf(stderr, "[sparsemla] T=%lld H=%lld Dqk=%lld K=%lld kv=%s splits=%d rows/split=%d\n",
+            (long long)T, (long long)H, (long long)Dqk, (long long)K, kv_dtype ? "e4m3" : "bf16",
+            plan.S, plan.rps);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess)
+    return fail(SMLA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  e = smla::launch_fwd(p, kv_dtype == SMLA_KV_FP8_E4M3, (int)Dqk, s);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "forward kernel launch: %s", hipGetErrorString(e));
+  if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess)
+    return fail(SMLA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  if (plan.S > 1) {
+    e = smla::launch_combine(p, s);
+    if (e != hipSuccess) return fail(SMLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+  }
+  return SMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+smla_status_t sparse_mla_fwd(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t q_stride_t,
+                             int64_t q_stride_h, const void* kv_pool, int32_t kv_dtype,
+                             int64_t num_blocks, int64_t block_size, const int32_t* topk_idx,
+                             int64_t K, int64_t idx_stride_t, float sm_scale, float kv_scale,
+                             void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return fwd_impl(q, T, H, Dqk, q_stride_t, q_stride_h, kv_pool, kv_dtype, num_blocks, block_size,
+                  topk_idx, K, idx_stride_t, sm_scale, kv_scale, out, lse, workspace,
+                  workspace_bytes, stream, nullptr);
+}
+
+smla_status_t sparse_mla_fwd_ex(const void* q, int64_t T, int64_t H, int64_t Dqk,
+                                int64_t q_stride_t, int64_t q_stride_h, const void* kv_pool,
+                                int32_t kv_dtype, int64_t num_blocks, int64_t block_size,
+                                const int32_t* topk_idx, int64_t K, int64_t idx_stride_t,
+                                float sm_scale, float kv_scale, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                const smla_options_t* opts) {
+  return fwd_impl(q, T, H, Dqk, q_stride_t, q_stride_h, kv_pool, kv_dtype, num_blocks, block_size,
+                  topk_idx, K, idx_stride_t, sm_scale, kv_scale, out, lse, workspace,
+                  workspace_bytes, stream, opts);
+}
+
+int32_t sparse_mla_num_splits(int64_t T, int64_t H, int64_t K, int64_t Dqk, int32_t kv_dtype,
+                              int32_t num_splits) {
+  g_last_error.clear();
+  if (check_sizes(T, H, K, Dqk, kv_dtype) != SMLA_OK) return 0;
+  Plan plan;
+  if (make_plan(T, H, K, num_splits, &plan) != SMLA_OK) return 0;
+  return plan.S;
+}
+
+size_t sparse_mla_workspace_bytes(int64_t T, int64_t H, int64_t K, int64_t Dqk, int32_t kv_dtype,
+                                  int32_t num_splits) {
+  g_last_error.clear();
+  if (check_sizes(T, H, K, Dqk, kv_dtype) != SMLA_OK) return (size_t)-1;
+  Plan plan;
+  if (make_plan(T, H, K, num_splits, &plan) != SMLA_OK) return (size_t)-1;
+  return plan.ws_bytes;
+}
+
+smla_status_t sparse_mla_quantize_q_fp8(const void* q, int64_t T, int64_t H, int64_t Dqk,
+                                        int64_t q_stride_t, int64_t q_stride_h, uint8_t* codes,
+                                        float* scales, void* stream) {
+  g_last_error.clear();
+  smla_status_t st = check_sizes(T, H, 0, Dqk, SMLA_KV_FP8_E4M3);
+  if (st != SMLA_OK) return st;
+  if (q_stride_t < 0 || q_stride_h < 0) return fail(SMLA_ERR_SHAPE, "negative stride");
+  if (T == 0) return SMLA_OK;
+  if (!q || !codes || !scales) return fail(SMLA_ERR_NULL, "null pointer (q, codes, scales)");
+  if (!aligned(q, 16) || q_stride_t % 8 || q_stride_h % 8)
+    return fail(SMLA_ERR_ALIGN, "q must be 16-byte aligned with strides that are multiples of 8 elements");
+  if (!aligned(codes, 8) || !aligned(scales, 4))
+    return fail(SMLA_ERR_ALIGN, "codes must be 8-byte and scales 4-byte aligned");
+  hipError_t e = smla::launch_quantize_q(static_cast<const uint16_t*>(q), q_stride_t, q_stride_h,
+                                         (int32_t)T, (int32_t)H, (int)Dqk, codes, scales,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "quantize kernel launch: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+const char* sparse_mla_status_string(smla_status_t status) {
+  switch (status) {
+    case SMLA_OK: return "ok";
+    case SMLA_ERR_NULL: return "null pointer";
+    case SMLA_ERR_SHAPE: return "bad shape or stride";
+    case SMLA_ERR_DTYPE: return "unknown dtype";
+    case SMLA_ERR_ALIGN: return "misaligned pointer or stride";
+    case SMLA_ERR_INVALID_ARG: return "invalid argument";
+    case SMLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SMLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SMLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* sparse_mla_last_error(void) { return g_last_error.c_str(); }
+
+int32_t sparse_mla_abi_version(void) { return SMLA_ABI_VERSION; }
+
+}  // extern "C"

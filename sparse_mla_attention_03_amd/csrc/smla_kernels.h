@@ -1,0 +1,38 @@
+// smla_kernels.h -- host-side view of the libsparsemla kernels (launch wrappers).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+constexpr int kDV = 512;        // V / out width
+constexpr int kBK = 64;         // top-k entries (gathered rows) per pipeline tile
+constexpr int kThreads = 256;   // 4 wavefronts per workgroup
+
+struct FwdParams {
+  const uint16_t* q;            // bf16 [T, H, Dqk], strides in elements
+  int64_t q_st, q_sh;
+  const uint8_t* kv;            // [N, Dqk] rows, bf16 or e4m3
+  int64_t N;                    // number of slots
+  const int32_t* idx;           // [T, K], row stride idx_st
+  int64_t idx_st;
+  int32_t T, H, K;
+  int32_t S;                    // split-K factor (1 = write out/lse directly)
+  int32_t rps;                  // top-k entries per split, multiple of kBK
+  float sm_scale, kv_scale;
+  uint16_t* out;                // bf16 [T, H, 512]
+  float* lse;                   // fp32 [T, H]
+  float* part_o;                // fp32 [S, T, H, 512] (S > 1)
+  float* part_lse;              // fp32 [S, T, H]      (S > 1)
+};
+
+// Heads per workgroup for a head count (a multiple of 16).
+inline int heads_per_workgroup(int64_t H) { return (H % 64 == 0) ? 64 : (H % 32 == 0) ? 32 : 16; }
+
+hipError_t launch_fwd(const FwdParams& p, bool kv_fp8, int dqk, hipStream_t stream);
+hipError_t launch_combine(const FwdParams& p, hipStream_t stream);
+hipError_t launch_quantize_q(const uint16_t* q, int64_t q_st, int64_t q_sh, int32_t T, int32_t H,
+                             int dqk, uint8_t* codes, float* scales, hipStream_t stream);
+
+}  // namespace smla

@@ -1,0 +1,134 @@
+"""The C ABI without a GPU: exports, status strings, host-side validation.
+
+Every error path here is decided on the host before any HIP call, so these
+run on a machine with no GPU; nothing is launched.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from sparse_mla_attention_03_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_mla.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, INVALID, UNSUP, WS, HIP = range(9)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_mla_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("sparse_mla_fwd", "sparse_mla_fwd_ex", "sparse_mla_workspace_bytes",
+              "sparse_mla_num_splits", "sparse_mla_quantize_q_fp8", "sparse_mla_status_string",
+              "sparse_mla_last_error", "sparse_mla_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.sparse_mla_abi_version() == 1
+    seen = set()
+    for st in range(9):
+        s = binding.sparse_mla_status_string(st)
+        assert s and s not in seen
+        seen.add(s)
+    assert binding.sparse_mla_status_string(99) == "unknown status"
+
+
+# a fake, 256-byte aligned device address: never dereferenced (validation fails
+# or T == 0 returns before any launch)
+P = 0x7F0000000000
+
+
+def call(lib, q=P, T=4, H=16, D=512, qst=16 * 512, qsh=512, kv=P, dt=0, nb=16, bs=64,
+         idx=P, K=128, ist=128, sm=0.04, kvs=1.0, out=P, lse=P, ws=None, wsb=0, splits=1,
+         reserved=0, events=None):
+    opts = binding.Options()
+    opts.num_splits = splits
+    opts.reserved[0] = reserved
+    if events:
+        opts.kernel_events[0], opts.kernel_events[1] = events
+    st = lib.sparse_mla_fwd_ex(q, T, H, D, qst, qsh, kv, dt, nb, bs, idx, K, ist, sm, kvs, out,
+                               lse, ws, wsb, None, ctypes.byref(opts))
+    return st, binding.sparse_mla_last_error()
+
+
+def test_empty_batch_is_a_noop(lib):
+    assert call(lib, T=0, q=None, kv=None, idx=None, out=None, lse=None)[0] == OK
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), NULL, "null"),
+    (dict(out=None), NULL, "null"),
+    (dict(lse=None), NULL, "null"),
+    (dict(idx=None), NULL, "null"),
+    (dict(H=24), UNSUP, "H=24"),
+    (dict(H=0), SHAPE, "bad sizes"),
+    (dict(D=320), UNSUP, "Dqk=320"),
+    (dict(dt=2), DTYPE, "dtype"),
+    (dict(T=-1), SHAPE, "bad sizes"),
+    (dict(K=-5), SHAPE, "bad sizes"),
+    (dict(bs=0), SHAPE, "pool"),
+    (dict(nb=-1), SHAPE, "pool"),
+    (dict(qsh=-512), SHAPE, "stride"),
+    (dict(q=P + 2), ALIGN, "q must"),
+    (dict(qsh=516), ALIGN, "q must"),
+    (dict(kv=P + 8), ALIGN, "kv_pool"),
+    (dict(out=P + 4), ALIGN, "out"),
+    (dict(lse=P + 2), ALIGN, "lse"),
+    (dict(sm=math.inf), INVALID, "finite"),
+    (dict(kvs=math.nan), INVALID, "finite"),
+    (dict(splits=65), INVALID, "num_splits"),
+    (dict(splits=-1), INVALID, "num_splits"),
+    (dict(reserved=3), INVALID, "reserved"),
+    (dict(events=(P, None)), INVALID, "kernel_events"),
+    (dict(splits=2), WS, "workspace"),
+    (dict(splits=2, ws=P, wsb=100), WS, "workspace"),
+    (dict(splits=2, ws=P + 4, wsb=1 << 30), ALIGN, "workspace"),
+])
+def test_validation_errors(lib, kw, status, needle):
+    st, msg = call(lib, **kw)
+    assert st == status, (st, msg)
+    assert needle in msg
+
+
+def test_workspace_and_split_planning_explicit(lib):
+    # explicit split counts need no device query
+    assert binding.sparse_mla_workspace_bytes(32, 16, 2048, 512, 0, 1) == 0
+    assert binding.sparse_mla_workspace_bytes(32, 16, 2048, 512, 0, 8) == 8 * 32 * 16 * 513 * 4
+    # never more splits than 64-entry tiles; empty splits are dropped
+    assert binding.sparse_mla_num_splits(4, 16, 128, 512, 0, 8) == 2
+    assert binding.sparse_mla_num_splits(4, 16, 200, 512, 0, 3) == 2   # 4 tiles -> 2+2
+    assert binding.sparse_mla_num_splits(4, 16, 0, 512, 0, 5) == 1
+    with pytest.raises(binding.SparseMLAError):
+        binding.sparse_mla_num_splits(4, 24, 128, 512, 0, 1)
+    with pytest.raises(binding.SparseMLAError):
+        binding.sparse_mla_workspace_bytes(4, 16, 128, 600, 0, 1)
+
+
+def test_quantize_entry_validation(lib):
+    st = lib.sparse_mla_quantize_q_fp8(None, 2, 16, 512, 8192, 512, P, P, None)
+    assert st == NULL
+    st = lib.sparse_mla_quantize_q_fp8(P, 2, 20, 512, 8192, 512, P, P, None)
+    assert st == UNSUP
+    assert lib.sparse_mla_quantize_q_fp8(None, 0, 16, 512, 0, 0, None, None, None) == OK
