@@ -78,7 +78,8 @@ smla_status_t check_sizes(int64_t T, int64_t H, int64_t K, int64_t Dqk, int32_t 
 }
 
 // Split-K choice: enough (token, head group, split) units to give every
-// compute unit one workgroup, never more splits than 64-entry tiles.
+// compute unit one workgroup, but at least 256 list entries per split (below
+// that a split's fixed cost and the combine outweigh the parallelism gained).
 smla_status_t make_plan(int64_t T, int64_t H, int64_t K, int32_t req, Plan* plan) {
   const int64_t tiles = (K + smla::kBK - 1) / smla::kBK;
   const int64_t HG = H / smla::heads_per_workgroup(H);
@@ -93,6 +94,8 @@ smla_status_t make_plan(int64_t T, int64_t H, int64_t K, int32_t req, Plan* plan
     if (st != SMLA_OK) return st;
     const int64_t units = T * HG;
     if (units < cus) S = (cus + units - 1) / units;
+    const int64_t max_by_size = tiles / 4;   // 4 x 64 entries per split at least
+    if (S > max_by_size) S = max_by_size > 0 ? max_by_size : 1;
   }
   if (S > tiles) S = tiles > 0 ? tiles : 1;
   if (S > SMLA_MAX_SPLITS) S = SMLA_MAX_SPLITS;

@@ -28,6 +28,13 @@ __device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x16_bf16: as above with 4 k-values per lane (k-slot l/16).
+__device__ __forceinline__ f32x4 mfma_bf16_k16(const u32x2& a, const u32x2& b, const f32x4& c) {
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
+                                                   __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+}
+
 // v_mfma_f32_16x16x128_f8f6f4 with both operands OCP e4m3 (format code 0):
 // same lane roles as above, 32 fp8 k-values per lane.
 __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const f32x4& c) {
@@ -46,6 +53,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 // four OCP e4m3 codes (one dword) -> four bf16 (exact: every e4m3 value is a bf16)
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t codes) {
+  // v_cvt_scalef32_pk_bf16_fp8 with scale 1
   bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false);
   bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true);
   return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
@@ -58,6 +66,24 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, f
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
+
+// low / high bf16 halves of two words -> one word (a's half low, b's half high),
+// one v_perm_b32 each: bytes 0-3 select from a, 4-7 from b
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// ---- buffer loads ---------------------------------------------------------------
+// Structured buffer: record i of `stride` bytes at base + i*stride.  A record
+// index >= num_records is out of range: the load returns zeros and touches no
+// memory, which is how padding entries of a top-k list are gathered.
+__device__ u32x4 struct_load_b128(__amdgpu_buffer_rsrc_t rsrc, int vindex, int voffset, int soffset,
+                                  int aux) __asm("llvm.amdgcn.struct.ptr.buffer.load.v4i32");
+
+constexpr int kBufferRsrcWord3 = 0x00020000;   // 32-bit untyped data format
 
 // ---- wavefront reductions (64 lanes) ------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
@@ -85,12 +111,19 @@ __device__ float q_tile_amax(const uint16_t* __restrict__ qtok, int64_t q_sh, in
   constexpr int CPR = D / 8;   // 16-byte chunks per head row
   const int n = (qh1 - qh0) * CPR;
   float m = 0.0f;
-  for (int c = threadIdx.x; c < n; c += blockDim.x) {
-    const int hh = qh0 + c / CPR, cc = c % CPR;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(qtok + (int64_t)hh * q_sh + cc * 8);
+  // four independent loads per step (indices clamped, so no guard serialises them)
+  for (int c0 = threadIdx.x; c0 < n; c0 += 4 * blockDim.x) {
+    u32x4 v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
+    for (int j = 0; j < 4; ++j) {
+      const int c = min(c0 + j * (int)blockDim.x, n - 1);
+      v[j] = *reinterpret_cast<const u32x4*>(qtok + (int64_t)(qh0 + c / CPR) * q_sh + (c % CPR) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[j][i])), fabsf(bf16_hi(v[j][i]))));
   }
   m = wave_max(m);
   const int nw = blockDim.x >> 6;

@@ -1,30 +1,33 @@
 // smla_kernels.hip -- gfx950 kernels of libsparsemla.
 //
-// One workgroup (4 wavefronts) owns one unit of work: a query token t, a head
-// group of HT heads (16, 32 or 64) and a split s, i.e. a contiguous range of
-// t's top-k list.  It walks that range in tiles of 64 entries:
+// A workgroup (4 wavefronts) owns one unit of work: a query token t, a group
+// of heads and a split s (a contiguous range of t's top-k list).  Two kernels
+// share the building blocks:
 //
-//   gather   every wave fetches 16 of the tile's rows with 16-byte loads (one
-//            64-lane load covers a whole 1 KiB bf16 row) into registers, then
-//            writes them to an LDS stage whose 16-byte chunks are rotated by
-//            the row number (conflict-free column reads).  Invalid entries
-//            (padding, out of range, past the split) read a zero row instead of
-//            the pool.  Two LDS stages plus one tile in flight in registers.
+//   smla_rows_kernel   16-head groups (H = 16, 48, 80, ...).  Each wave streams
+//                      its own 16-row tiles of the split (tiles w, w+4, ...)
+//                      with two tiles in flight in registers and a private LDS
+//                      slot, so the loop has no workgroup barrier; the four
+//                      waves merge their (max, sum, O) once at the end.
+//   smla_tiles_kernel  32- or 64-head groups (H a multiple of 32).  All waves
+//                      share each gathered 64-row tile in LDS, so a row is read
+//                      from HBM once for up to 64 heads.
+//
+// Per gathered row both run the same steps:
+//   gather   16-byte loads (one 64-lane load covers a 1 KiB bf16 row) into
+//            registers, then into LDS with 16-byte chunks rotated by the row
+//            number (conflict-free column reads).  Invalid entries (padding,
+//            out of range, past the split) read a zero row, never the pool.
 //   QK^T     v_mfma_f32_16x16x32_bf16 (bf16 KV) or v_mfma_f32_16x16x128_f8f6f4
 //            (e4m3 KV, q quantised per tile), rows x heads, fp32 accumulation.
-//   softmax  online, in registers, log2 domain; each lane owns one head and 16
-//            of the tile's rows, so the only cross-lane steps are a max over
-//            four lanes per tile and the final sum.
-//   PV       V = the first 512 columns of the same LDS rows, read 8 rows x 8
-//            columns per lane and transposed in registers into the MFMA
+//   softmax  online, in registers, log2 domain; a lane owns one head and a
+//            few rows, so the only cross-lane step is a max over 4 lanes.
+//   PV       V = the first 512 columns of the same LDS rows, read 4 or 8 rows x
+//            8 columns per lane and transposed in registers into the MFMA
 //            operand; O^T[dim][head] accumulates in fp32.
 //   epilogue S == 1: out = bf16(O * kv_scale / l), lse = ln(sum exp).  S > 1:
 //            normalised fp32 partials + lse per split, merged by the combine
 //            kernel (log-sum-exp weights).
-//
-// Waves of a head group split the work two ways: with WD = 4 / (HT/16) waves
-// per 16-head tile, each wave computes QK for 64/WD rows (exchanged through
-// LDS) and PV for 512/WD output columns.
 #include <type_traits>
 
 #include "smla_device.h"
@@ -68,8 +71,32 @@ __device__ __forceinline__ u32x2 lds_read8(const uint8_t* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }
 
+// Slot ids of an n-row tile: lane j (j < n) loads entry k0 + j of the list,
+// -1 past the end of the split.  One vector load per tile, issued ahead of use.
+template <int n = 16>
+__device__ __forceinline__ int load_tile_idx(const int32_t* idx_t, int k0, int kend, int lane) {
+  const int k = k0 + (lane & (n - 1));
+  return (lane < n && k < kend) ? idx_t[k] : -1;
+}
+
+// Row addresses of that tile (wave-uniform): invalid entries (padding, out of
+// range) point at the zero row instead of the pool.  Returns the validity mask.
+template <int ROW, int n = 16>
+__device__ __forceinline__ uint32_t tile_rows(int vidx, const uint8_t* kv, int64_t N,
+                                              const uint8_t* zero_row, const uint8_t* (&rp)[n]) {
+  uint32_t vm = 0;
+#pragma unroll
+  for (int j = 0; j < n; ++j) {
+    const int sl = __builtin_amdgcn_readlane(vidx, j);
+    const bool ok = sl >= 0 && (int64_t)sl < N;
+    rp[j] = ok ? kv + (int64_t)sl * ROW : zero_row;
+    vm |= ok ? (1u << j) : 0u;
+  }
+  return vm;
+}
+
 template <bool KV8, int DQK, int HT>
-__global__ __launch_bounds__(kThreads, 1) void smla_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
   using G = Geom<KV8, DQK>;
   constexpr int WH = HT / 16;          // 16-head tiles per workgroup
   constexpr int WD = 4 / WH;           // waves per head tile
@@ -163,19 +190,10 @@ __global__ __launch_bounds__(kThreads, 1) void smla_fwd_kernel(FwdParams p) {
   uint32_t ld_mask = 0;
   const uint8_t* zero_row = g_zero_row;
 
-  auto issue = [&](int tile) {
-    const int k0 = kbeg + tile * kBK + 16 * wave;
+  auto tile_k0 = [&](int tile) { return kbeg + tile * kBK + 16 * wave; };
+  auto issue = [&](int vidx) {
     const uint8_t* rp[16];
-    uint32_t vm = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int k = k0 + j;
-      const int64_t slot = (k < kend) ? (int64_t)idx_t[k] : -1;
-      const bool ok = slot >= 0 && slot < p.N;
-      rp[j] = ok ? p.kv + slot * G::ROW : zero_row;
-      vm |= ok ? (1u << j) : 0u;
-    }
-    ld_mask = vm;
+    ld_mask = tile_rows<G::ROW>(vidx, p.kv, p.N, zero_row, rp);
     if constexpr (!KV8) {
 #pragma unroll
       for (int j = 0; j < 16; ++j)
@@ -235,8 +253,14 @@ __global__ __launch_bounds__(kThreads, 1) void smla_fwd_kernel(FwdParams p) {
 
   float* sx = reinterpret_cast<float*>(smem + RING);
 
-  if (ntiles > 0) { issue(0); commit(0); }
-  if (ntiles > 1) issue(1);
+  // slot ids run two tiles ahead of the row loads that use them
+  int vidx_next = load_tile_idx(idx_t, tile_k0(0), kend, lane);
+  int vidx_next2 = load_tile_idx(idx_t, tile_k0(1), kend, lane);
+  if (ntiles > 0) { issue(vidx_next); commit(0); }
+  vidx_next = vidx_next2;
+  vidx_next2 = load_tile_idx(idx_t, tile_k0(2), kend, lane);
+  if (ntiles > 1) issue(vidx_next);
+  vidx_next = vidx_next2;
 
   for (int it = 0; it < ntiles; ++it) {
     const int stage = it & 1;
@@ -327,8 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_fwd_kernel(FwdParams p) {
       const float e3 = __builtin_amdgcn_exp2f(sv[b][3] - m_use);
       pk[b][0] = pack_bf16(e0, e1);
       pk[b][1] = pack_bf16(e2, e3);
-      // the denominator sums exactly the bf16 weights PV multiplies by
-      psum += (bf16_lo(pk[b][0]) + bf16_hi(pk[b][0])) + (bf16_lo(pk[b][1]) + bf16_hi(pk[b][1]));
+      psum += (e0 + e1) + (e2 + e3);   // fp32 weights: the denominator and lse stay fp32-accurate
     }
     l_run = l_run * alpha + psum;
 #pragma unroll
@@ -375,7 +398,9 @@ __global__ __launch_bounds__(kThreads, 1) void smla_fwd_kernel(FwdParams p) {
     // ---- refill: tile it+1 -> the other stage (free since the barrier above),
     // then start fetching tile it+2 into registers
     if (it + 1 < ntiles) commit(stage ^ 1);
-    if (it + 2 < ntiles) issue(it + 2);
+    const int vidx_after = load_tile_idx(idx_t, tile_k0(it + 3), kend, lane);
+    if (it + 2 < ntiles) issue(vidx_next);
+    vidx_next = vidx_after;
   }
 
   // ---- epilogue ---------------------------------------------------------------
@@ -417,28 +442,443 @@ __global__ __launch_bounds__(kThreads, 1) void smla_fwd_kernel(FwdParams p) {
   }
 }
 
+// ---- 16-head groups: every wave streams its own tiles ---------------------------
+
+constexpr float kSlack = 8.0f;   // log2 headroom of the lazily rescaled running max
+
+template <bool KV8, int DQK, int TR>
+__global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
+  using G = Geom<KV8, DQK>;
+  static_assert(TR == 16 || TR == 32, "a wave tile is one or two 16-row blocks");
+  constexpr int NB = TR / 16;                             // 16-row blocks per tile
+  constexpr int WMAIN = TR * G::MAIN;
+  constexpr int WSLOT = TR * (G::MAIN + G::TAIL);         // a wave's LDS slot
+  // Gather layout: one 64-lane load covers 8 rows x 128 bytes (8 lanes per full
+  // cache line); lane l takes row 8*grp + (l >> 3), chunk (l & 7) + 8*i.
+  constexpr int NGRP = TR / 8;                            // 8-row groups per tile
+  constexpr int NCI = G::MCH / 8;                         // 128-byte pieces of a row's V part
+  constexpr int NLDM = NGRP * NCI;                        // main loads per tile
+  constexpr int TROWS = (G::TCH == 8) ? 8 : 16;           // RoPE part: rows per load
+  constexpr int NLDT = G::TCH ? TR / TROWS : 0;           // RoPE loads per tile
+  constexpr int NLD = NLDM + NLDT;
+  constexpr int QROW = DQK * (KV8 ? 1 : 2) + 16;          // padded q row (no bank conflicts)
+  constexpr int QBYTES = 16 * QROW;                       // the group's q (B operand of QK^T)
+  constexpr int OPAD = kDV + 4;                           // padded fp32 row of the merge buffer
+  constexpr int MERGE = 4 * 16 * OPAD * 4;                // the four waves' O (after the loop)
+  constexpr int SMEM = (4 * WSLOT + QBYTES > MERGE) ? 4 * WSLOT + QBYTES : MERGE;
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  __shared__ float s_m[4][16], s_l[4][16];
+  __shared__ float s_red[4];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int m16 = lane & 15;
+  const int g = lane >> 4;
+
+  // workgroup -> (token, split, 16-head group), head groups of a unit 8 ids apart
+  const int HG = p.H / 16;
+  const int L = blockIdx.x;
+  const int hg = (L >> 3) % HG;
+  const int u = ((L >> 3) / HG) * 8 + (L & 7);
+  if (u >= p.T * p.S) return;
+  const int t = u / p.S;
+  const int s = u - t * p.S;
+  const int h0 = hg * 16;
+  const int kbeg = s * p.rps;
+  const int kend = min(kbeg + p.rps, p.K);
+  const int ntile = kend > kbeg ? (kend - kbeg + TR - 1) / TR : 0;
+  const int nt = ntile > wave ? (ntile - wave + 3) / 4 : 0;   // this wave's tiles: wave + 4i
+
+  const int head = h0 + m16;
+  const uint16_t* qtok = p.q + (int64_t)t * p.q_st;
+  const int32_t* idx_t = p.idx + (int64_t)t * p.idx_st;
+
+  // the pool as a structured buffer of N rows: out-of-range indices read zeros
+  const uint32_t nrec = (uint32_t)min(p.N, (int64_t)0xffffffffLL);
+  const __amdgpu_buffer_rsrc_t pool =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, (short)G::ROW, (int)nrec, kBufferRsrcWord3);
+
+  uint8_t* slot = smem + wave * WSLOT;   // this wave's tile, rows 0 .. TR-1
+  // 16-byte chunk c of tile row r sits at chunk position c ^ (r & 15) (V part)
+  // or c ^ (r & (TCH-1)) (RoPE part): conflict-free row and column accesses.
+  auto off_main = [](int r, int c) { return r * G::MAIN + 16 * (c ^ (r & 15)); };
+  auto off_tail = [](int r, int c) { return WMAIN + r * G::TAIL + 16 * (c ^ (r & (G::TCH - 1))); };
+
+  // ---- slot ids of a tile: lane j < TR holds entry k0 + j of the list, or -1
+  // (padding, out of range, past the split: all read zeros).  Returns the
+  // record index every lane gathers for each 8-row group via ds_bpermute.
+  auto tile_k0 = [&](int i) { return kbeg + TR * (wave + 4 * i); };
+  auto load_idx = [&](int i) -> int {
+    const int k = tile_k0(i) + (lane & (TR - 1));
+    return (lane < TR && k < kend) ? idx_t[k] : -1;
+  };
+  auto issue = [&](u32x4 (&ld)[NLD], uint32_t& vmask, int vslot) {
+    const bool ok = lane < TR && vslot >= 0 && (int64_t)vslot < p.N;
+    vmask = (uint32_t)__ballot(ok);
+    const int rec = ok ? vslot : -1;   // -1 = 0xffffffff >= any record count
+#pragma unroll
+    for (int grp = 0; grp < NGRP; ++grp) {
+      const int ri = __shfl(rec, 8 * grp + (lane >> 3));
+#pragma unroll
+      for (int i = 0; i < NCI; ++i)
+        ld[grp * NCI + i] = struct_load_b128(pool, ri, 16 * (lane & 7) + 128 * i, 0, 0);
+    }
+    if constexpr (NLDT > 0) {
+      // RoPE part: 8 rows x 8 chunks (bf16) or 16 rows x 4 chunks (e4m3) per load
+#pragma unroll
+      for (int j = 0; j < NLDT; ++j) {
+        const int ri = __shfl(rec, TROWS * j + lane / G::TCH);
+        ld[NLDM + j] = struct_load_b128(pool, ri, G::MAIN + 16 * (lane % G::TCH), 0, 0);
+      }
+    }
+  };
+
+  // lane bases of the commit: row (l>>3) of a group, chunk (l&7) + 8i lands at
+  // position ((l&7) ^ (l>>3)) + 8 (i ^ (grp&1)), because row & 15 = 8 (grp&1) + (l>>3)
+  const int cm_base = (lane >> 3) * G::MAIN + 16 * ((lane & 7) ^ (lane >> 3));
+  auto commit = [&](const u32x4 (&ld)[NLD]) {
+#pragma unroll
+    for (int grp = 0; grp < NGRP; ++grp)
+#pragma unroll
+      for (int i = 0; i < NCI; ++i)
+        *reinterpret_cast<u32x4*>(slot + cm_base + 8 * grp * G::MAIN + 128 * (i ^ (grp & 1))) =
+            ld[grp * NCI + i];
+    if constexpr (NLDT > 0) {
+#pragma unroll
+      for (int j = 0; j < NLDT; ++j)
+        *reinterpret_cast<u32x4*>(slot + off_tail(TROWS * j + lane / G::TCH, lane % G::TCH)) = ld[NLDM + j];
+    }
+  };
+
+  // ---- the group's 16 q rows: every thread loads its chunks at once (indices
+  // clamped instead of guarded, so all loads are in flight together)
+  constexpr int CPR = DQK / 8;                              // 16-byte chunks per head row
+  constexpr int NQ = (16 * CPR + kThreads - 1) / kThreads;  // chunks per thread
+  u32x4 qv[NQ];
+#pragma unroll
+  for (int r = 0; r < NQ; ++r) {
+    const int c = min(tid + r * kThreads, 16 * CPR - 1), hh = c / CPR, cc = c - hh * CPR;
+    qv[r] = *reinterpret_cast<const u32x4*>(qtok + (int64_t)(h0 + hh) * p.q_sh + cc * 8);
+  }
+
+  // ---- first tile: slot ids, then its rows, before q is staged (overlaps the latencies)
+  u32x4 ldA[NLD];
+  uint32_t vmA = 0;
+  int vidx_next = load_idx(0);
+  int vidx_next2 = load_idx(1);
+  issue(ldA, vmA, vidx_next);   // unconditional: past the split every row reads as zero
+  vidx_next = vidx_next2;
+
+  // ---- q operand (B of QK^T), staged once in LDS for the four waves: bf16 rows,
+  // or e4m3 codes of the per-tile quantised q
+  uint8_t* qs = smem + 4 * WSLOT;
+  float c2;
+  if constexpr (!KV8) {
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+      const int c = tid + r * kThreads, hh = c / CPR, cc = c - hh * CPR;
+      if (c < 16 * CPR) *reinterpret_cast<u32x4*>(qs + hh * QROW + cc * 16) = qv[r];
+    }
+    c2 = p.sm_scale * p.kv_scale * kLog2e;
+  } else {
+    const int qt0 = (h0 / 64) * 64;
+    const int qt1 = min(qt0 + 64, p.H);
+    float amax;
+    if (qt1 - qt0 == 16) {
+      // the quantisation tile is exactly this head group: amax from the registers
+      float m = 0.0f;
+#pragma unroll
+      for (int r = 0; r < NQ; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          m = fmaxf(m, fmaxf(fabsf(bf16_lo(qv[r][i])), fabsf(bf16_hi(qv[r][i]))));
+      m = wave_max(m);
+      if (lane == 0) s_red[wave] = m;
+      __syncthreads();
+      amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    } else {
+      amax = q_tile_amax<DQK>(qtok, p.q_sh, qt0, qt1, s_red);
+    }
+    const float s_q = q_scale_from_amax(amax);
+    const float r_q = 1.0f / s_q;
+    auto quantize_into_lds = [&](auto fast) {
+#pragma unroll
+      for (int r = 0; r < NQ; ++r) {
+        const int c = tid + r * kThreads, hh = c / CPR, cc = c - hh * CPR;
+        if (c < 16 * CPR)
+          *reinterpret_cast<u32x2*>(qs + hh * QROW + cc * 8) = quantize_chunk<decltype(fast)::value>(qv[r], s_q, r_q);
+      }
+    };
+    if (q_tile_fast_div(amax)) quantize_into_lds(std::true_type{});
+    else quantize_into_lds(std::false_type{});
+    c2 = p.sm_scale * p.kv_scale * s_q * kLog2e;
+  }
+  __syncthreads();
+  // lane (head = m16, g): bf16 columns 32kb + 8g .. +8, or e4m3 columns 128kb + 32g .. +32
+  const uint8_t* qlane = qs + m16 * QROW;
+
+  // QK reads: row 16b + m16 (row & 15 = m16), chunk 4kb + g lands at
+  // 4 (kb ^ (m16>>2)) + (g ^ (m16&3)): four lane bases, one per kb mod 4
+  int qk_base[4];
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) qk_base[r4] = m16 * G::MAIN + 64 * (r4 ^ (m16 >> 2)) + 16 * (g ^ (m16 & 3));
+  // PV reads (bf16): row 16b + 4g + i, chunk m16 + 16a lands at 16a + (m16 ^ (4g + i))
+  int pv_base[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pv_base[i] = (4 * g + i) * G::MAIN + 16 * (m16 ^ (4 * g + i));
+
+  f32x4 O[4][8];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) O[a][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+
+  auto compute = [&](uint32_t vm) {
+    // QK^T: S^T[row][head] per 16-row block b, lane (head = m16, g) receives
+    // rows 16b + 4g .. 16b + 4g + 3
+    f32x4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const uint8_t* blk = slot + 16 * b * G::MAIN;
+      f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (!KV8) {
+#pragma unroll
+        for (int kb = 0; kb < G::NKB; ++kb) {
+          const u32x4 a = (kb < G::MCH / 4)
+                              ? lds_read16(blk + qk_base[kb & 3] + 256 * (kb >> 2))
+                              : lds_read16(slot + off_tail(16 * b + m16, 4 * kb + g - G::MCH));
+          a4 = mfma_bf16(a, lds_read16(qlane + (kb * 32 + 8 * g) * 2), a4);
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < G::NKB; ++kb) {
+          const int c = 8 * kb + 2 * g;
+          u32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
+          if (kb < G::MCH / 8) {
+            a0 = lds_read16(slot + off_main(16 * b + m16, c));
+            a1 = lds_read16(slot + off_main(16 * b + m16, c + 1));
+            b0 = lds_read16(qlane + 16 * c);
+            b1 = lds_read16(qlane + 16 * c + 16);
+          } else if (2 * g < G::TCH) {
+            a0 = lds_read16(slot + off_tail(16 * b + m16, c - G::MCH));
+            a1 = lds_read16(slot + off_tail(16 * b + m16, c - G::MCH + 1));
+            b0 = lds_read16(qlane + 16 * c);
+            b1 = lds_read16(qlane + 16 * c + 16);
+          }
+          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          const i32x8 bq = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                            (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+          a4 = mfma_fp8(a, bq, a4);
+        }
+      }
+      acc[b] = a4;
+    }
+    // online softmax over the tile's rows
+    float sv[NB][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[b][i] = ((vm >> (16 * b + 4 * g + i)) & 1u) ? acc[b][i] * c2 : -INFINITY;
+        mt = fmaxf(mt, sv[b][i]);
+      }
+    mt = group4_max(mt);
+    // m_run is a reference max that may lag the true one by up to kSlack, so
+    // exponents stay <= 2^kSlack and O is rescaled only when some head's
+    // scores outgrow it (after the first valid tile, rarely)
+    if (__ballot(mt > m_run + kSlack) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) O[a][e] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    uint32_t pk[NB][2];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float e0 = __builtin_amdgcn_exp2f(sv[b][0] - m_use);
+      const float e1 = __builtin_amdgcn_exp2f(sv[b][1] - m_use);
+      const float e2 = __builtin_amdgcn_exp2f(sv[b][2] - m_use);
+      const float e3 = __builtin_amdgcn_exp2f(sv[b][3] - m_use);
+      l_run += (e0 + e1) + (e2 + e3);
+      pk[b][0] = pack_bf16(e0, e1);
+      pk[b][1] = pack_bf16(e2, e3);
+    }
+    // PV: O^T[dim][head] += V^T[dim][row] P^T[row][head]; k-slot g holds rows
+    // 16b + 4g + i for every block b (i = 0..3), in the same order on both sides
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int c = m16 + 16 * a;   // 8-column chunk of this lane
+      u32x4 R[4 * NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * b + 4 * g + i;
+          if constexpr (!KV8) {
+            R[4 * b + i] = lds_read16(slot + pv_base[i] + 16 * b * G::MAIN + 256 * a);
+          } else {
+            const u32x2 raw = lds_read8(slot + off_main(row, c >> 1) + 8 * (c & 1));
+            const u32x2 lo = e4m3x4_to_bf16x4(raw[0]);
+            const u32x2 hi = e4m3x4_to_bf16x4(raw[1]);
+            R[4 * b + i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          }
+        }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        if constexpr (NB == 1) {
+          const u32x2 pf = {pk[0][0], pk[0][1]};
+          const u32x2 A = (e & 1) ? u32x2{pack_hi(R[0][w], R[1][w]), pack_hi(R[2][w], R[3][w])}
+                                  : u32x2{pack_lo(R[0][w], R[1][w]), pack_lo(R[2][w], R[3][w])};
+          O[a][e] = mfma_bf16_k16(A, pf, O[a][e]);
+        } else {
+          const u32x4 pf = {pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
+          u32x4 A;
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            A[x] = (e & 1) ? pack_hi(R[2 * x][w], R[2 * x + 1][w]) : pack_lo(R[2 * x][w], R[2 * x + 1][w]);
+          O[a][e] = mfma_bf16(A, pf, O[a][e]);
+        }
+      }
+    }
+  };
+
+  // ---- main loop: one tile in flight in registers while the previous one
+  // computes from LDS; slot ids run two tiles ahead of the loads that use them
+  for (int i = 0; i < nt; ++i) {
+    commit(ldA);
+    const uint32_t va = vmA;
+    const int vidx_after = load_idx(i + 2);
+    if (i + 1 < nt) issue(ldA, vmA, vidx_next);   // none past the end: the merge barrier would wait for it
+    vidx_next = vidx_after;
+    compute(va);
+  }
+
+  // ---- merge the four waves: each writes its raw O (straight from the
+  // accumulators) and (max, sum) to LDS; wave w then combines columns
+  // [128w, 128w + 128) of all four in a fixed order and writes them out
+  const float l_w = group4_sum(l_run);
+  __syncthreads();   // every wave is done with its slot; the merge reuses them
+  float* ob = reinterpret_cast<float*>(smem);
+  {
+    float* row = ob + (wave * 16 + m16) * OPAD;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        f32x4 v;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) { const int j = 4 * k + x; v[x] = O[a][j & 7][j >> 3]; }
+        *reinterpret_cast<f32x4*>(row + 128 * a + 32 * g + 4 * k) = v;
+      }
+  }
+  if (g == 0) { s_m[wave][m16] = m_run; s_l[wave][m16] = l_w; }
+  __syncthreads();
+  float M = s_m[0][m16];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) M = fmaxf(M, s_m[w][m16]);
+  float f[4], Lsum = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f[w] = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][m16] - M);
+    Lsum += f[w] * s_l[w][m16];
+  }
+  const bool any = Lsum > 0.0f;
+  const float scale = any ? p.kv_scale / Lsum : 0.0f;
+  const float lse_nat = any ? (M + __builtin_amdgcn_logf(Lsum)) * kLn2 : -INFINITY;
+  const int64_t th = (int64_t)t * p.H + head;
+  const int d0 = 128 * wave + 32 * g;   // this lane's 32 columns of head `head`
+  float acc[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float* src = ob + (w * 16 + m16) * OPAD + d0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * k);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) acc[4 * k + x] += f[w] * v[x];
+    }
+  }
+  if (p.S == 1) {
+    u32x4* dst = reinterpret_cast<u32x4*>(p.out + th * kDV + d0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      dst[k] = u32x4{pack_bf16(acc[8 * k] * scale, acc[8 * k + 1] * scale),
+                     pack_bf16(acc[8 * k + 2] * scale, acc[8 * k + 3] * scale),
+                     pack_bf16(acc[8 * k + 4] * scale, acc[8 * k + 5] * scale),
+                     pack_bf16(acc[8 * k + 6] * scale, acc[8 * k + 7] * scale)};
+  } else {
+    f32x4* dst = reinterpret_cast<f32x4*>(p.part_o + ((int64_t)s * p.T * p.H + th) * kDV + d0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      dst[k] = f32x4{acc[4 * k] * scale, acc[4 * k + 1] * scale, acc[4 * k + 2] * scale,
+                     acc[4 * k + 3] * scale};
+  }
+  if (wave == 0 && g == 0) {
+    if (p.S == 1) p.lse[th] = lse_nat;
+    else p.part_lse[(int64_t)s * p.T * p.H + th] = lse_nat;
+  }
+}
+
 // ---- split merge: out = sum_s w_s * O_s / sum_s w_s, w_s = exp(lse_s - max) ----
+// One (token, head) pair per 128 threads, 4 columns per thread.  The lse and
+// partial loads of up to 8 splits are issued together (an empty split's
+// partial is loaded but its weight selects zero), so a call costs one memory
+// round trip for S <= 8.
 __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
   const int64_t TH = (int64_t)p.T * p.H;
   const int64_t pair = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
   if (pair >= TH) return;
   const int d4 = (threadIdx.x & 127) * 4;
-  float M = -INFINITY;
-  for (int s = 0; s < p.S; ++s) M = fmaxf(M, p.part_lse[s * TH + pair]);
+  const float* pl = p.part_lse + pair;
+  const float* po = p.part_o + pair * kDV + d4;
+  constexpr int B = 8;
+  float M = -INFINITY, W = 0.0f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < p.S; s0 += B) {
+    float ls[B];
+    f32x4 v[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int sj = min(s0 + j, p.S - 1);
+      ls[j] = (s0 + j < p.S) ? pl[sj * TH] : -INFINITY;
+      v[j] = *reinterpret_cast<const f32x4*>(po + sj * TH * kDV);
+    }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < B; ++j) mb = fmaxf(mb, ls[j]);
+    if (mb == -INFINITY) continue;
+    // rescale what was accumulated so far to the new running max
+    const float r = __builtin_amdgcn_exp2f((M - mb) * kLog2e);
+    W *= r;
+    acc *= r;
+    M = mb;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const bool live = ls[j] != -INFINITY;
+      const float w = live ? __builtin_amdgcn_exp2f((ls[j] - M) * kLog2e) : 0.0f;
+      W += w;
+      acc += live ? w * v[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
   u32x2* dst = reinterpret_cast<u32x2*>(p.out + pair * kDV + d4);
   if (M == -INFINITY) {
     *dst = u32x2{0u, 0u};
     if (d4 == 0) p.lse[pair] = -INFINITY;
     return;
-  }
-  float W = 0.0f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < p.S; ++s) {
-    const float ls = p.part_lse[s * TH + pair];
-    if (ls == -INFINITY) continue;   // empty split: its partial is not read
-    const float w = __builtin_amdgcn_exp2f((ls - M) * kLog2e);
-    W += w;
-    acc += w * *reinterpret_cast<const f32x4*>(p.part_o + (s * TH + pair) * kDV + d4);
   }
   const float inv = 1.0f / W;
   *dst = u32x2{pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
@@ -482,9 +922,15 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 gd((unsigned)grid), bd(kThreads);
   switch (HT) {
-    case 16: hipLaunchKernelGGL((smla_fwd_kernel<KV8, DQK, 16>), gd, bd, 0, stream, p); break;
-    case 32: hipLaunchKernelGGL((smla_fwd_kernel<KV8, DQK, 32>), gd, bd, 0, stream, p); break;
-    default: hipLaunchKernelGGL((smla_fwd_kernel<KV8, DQK, 64>), gd, bd, 0, stream, p); break;
+    case 16:
+      // 32-row wave tiles where four of them plus q fit in LDS, else 16
+      if constexpr (KV8 || DQK == 512)
+        hipLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 32>), gd, bd, 0, stream, p);
+      else
+        hipLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 16>), gd, bd, 0, stream, p);
+      break;
+    case 32: hipLaunchKernelGGL((smla_tiles_kernel<KV8, DQK, 32>), gd, bd, 0, stream, p); break;
+    default: hipLaunchKernelGGL((smla_tiles_kernel<KV8, DQK, 64>), gd, bd, 0, stream, p); break;
   }
   return hipGetLastError();
 }
