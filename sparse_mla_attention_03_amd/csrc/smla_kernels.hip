@@ -833,6 +833,432 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   }
 }
 
+// ---- 64-head groups: score waves and output waves ---------------------------------
+// Eight waves.  Waves 0-3 (score waves) gather the tiles and own 16 heads each:
+// q stays in their registers as the B operand of QK^T, and they keep the online
+// softmax state and write P (bf16) to LDS.  Waves 4-7 (output waves) own 128
+// output columns of all 64 heads: O^T[128][64] in accumulators, with every V
+// fragment read from LDS feeding four head blocks.  Scoring runs one tile ahead
+// of PV, so each SIMD interleaves one score wave's and one output wave's MFMAs;
+// three LDS stages hold the tile being scored, the tile being multiplied and
+// the tile being filled, and one barrier per tile separates the phases.
+template <bool KV8, int DQK>
+__global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
+  using G = Geom<KV8, DQK>;
+  constexpr int TR = KV8 ? 64 : 32;        // rows per tile (36 KiB for Dqk = 576 either way)
+  constexpr int NB = TR / 16;              // 16-row QK blocks per tile
+  constexpr int NKS = TR / 32;             // 32-row PV k-steps per tile
+  constexpr int RPW = TR / 4;              // rows each score wave gathers (8 or 16)
+  constexpr int NGRP = RPW / 8;            // 8-row load groups
+  constexpr int NCI = G::MAIN / 128;       // 128-byte pieces of a row's V part
+  constexpr int NLDM = NGRP * NCI;
+  constexpr int TROWS = (G::TCH == 8) ? 8 : 16;      // RoPE part: rows per load
+  constexpr int NLDT = G::TCH ? RPW / TROWS : 0;
+  constexpr int NLD = NLDM + NLDT;
+  constexpr int TMAIN = TR * G::MAIN;
+  constexpr int STAGE = TR * G::ROW;
+  constexpr int PBUF = NKS * 4 * 64 * 16;  // P^T operands of one tile, lane order
+  static_assert(RPW % 8 == 0 && (G::TCH == 0 || RPW % TROWS == 0), "gather shape");
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * STAGE + 2 * PBUF];
+  __shared__ uint32_t s_mask[3][4];        // validity bits of each score wave's rows, per stage
+  __shared__ float s_alpha[2][64];         // rescale factor of O per head (when flagged)
+  __shared__ int s_flag[2][4];             // score wave w moved its heads' reference max
+  __shared__ float s_lfin[64];             // final softmax denominators
+  __shared__ float s_red[4];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int m16 = lane & 15;
+  const int g = lane >> 4;
+
+  // workgroup -> (token, split, 64-head group); the head groups of one
+  // (token, split) are 8 ids apart, on one XCD, so the second gather of a row
+  // is served by that XCD's L2
+  const int HG = p.H / 64;
+  const int L = blockIdx.x;
+  const int hg = (L >> 3) % HG;
+  const int u = ((L >> 3) / HG) * 8 + (L & 7);
+  if (u >= p.T * p.S) return;
+  const int t = u / p.S;
+  const int s = u - t * p.S;
+  const int h0 = hg * 64;
+  const int kbeg = s * p.rps;
+  const int kend = min(kbeg + p.rps, p.K);
+  const int nt = kend > kbeg ? (kend - kbeg + TR - 1) / TR : 0;
+  const uint16_t* qtok = p.q + (int64_t)t * p.q_st;
+  uint8_t* pbuf = smem + 3 * STAGE;
+
+  // 16-byte chunk c of tile row r sits at chunk position c ^ (r & 15) (V part)
+  // or c ^ (r & (TCH-1)) (RoPE part)
+  auto off_main = [](int r, int c) { return r * G::MAIN + 16 * (c ^ (r & 15)); };
+  auto off_tail = [](int r, int c) { return TMAIN + r * G::TAIL + 16 * (c ^ (r & (G::TCH - 1))); };
+
+  if (wave < 4) {
+    // =============================== score waves ===============================
+    const int qw = wave;                   // heads h0 + 16 qw + m16; gathers tile rows RPW*qw ..
+    const int head = h0 + 16 * qw + m16;
+    const uint16_t* qrow = qtok + (int64_t)head * p.q_sh;
+    const int32_t* idx_t = p.idx + (int64_t)t * p.idx_st;
+    const uint32_t nrec = (uint32_t)min(p.N, (int64_t)0xffffffffLL);
+    const __amdgpu_buffer_rsrc_t pool =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, (short)G::ROW, (int)nrec, kBufferRsrcWord3);
+
+    auto load_idx = [&](int j) -> int {
+      const int k = kbeg + TR * j + RPW * qw + (lane & (RPW - 1));
+      return (lane < RPW && k < kend) ? idx_t[k] : -1;
+    };
+    // rows of this wave's share of a tile: 8 rows x 128 bytes per load (lane l:
+    // row l >> 3, chunk l & 7 of a 128-byte piece); padding reads zeros
+    auto issue = [&](u32x4 (&ld)[NLD], uint32_t& vm, int vslot) {
+      const bool ok = lane < RPW && vslot >= 0 && (int64_t)vslot < p.N;
+      vm = (uint32_t)__ballot(ok);
+      const int rec = ok ? vslot : -1;
+#pragma unroll
+      for (int grp = 0; grp < NGRP; ++grp) {
+        const int ri = __shfl(rec, 8 * grp + (lane >> 3));
+#pragma unroll
+        for (int i = 0; i < NCI; ++i)
+          ld[grp * NCI + i] = struct_load_b128(pool, ri, 16 * (lane & 7) + 128 * i, 0, 0);
+      }
+      if constexpr (NLDT > 0) {
+#pragma unroll
+        for (int j = 0; j < NLDT; ++j) {
+          const int ri = __shfl(rec, TROWS * j + lane / G::TCH);
+          ld[NLDM + j] = struct_load_b128(pool, ri, G::MAIN + 16 * (lane % G::TCH), 0, 0);
+        }
+      }
+    };
+    // row rb + (l >> 3) has key 8x + (l >> 3), x = (rb >> 3) & 1, so chunk
+    // (l & 7) + 8i lands at ((l & 7) ^ (l >> 3)) + 8 (i ^ x)
+    const int cm_lane = (lane >> 3) * G::MAIN + 16 * ((lane & 7) ^ (lane >> 3));
+    auto commit = [&](int stage, const u32x4 (&ld)[NLD], uint32_t vm) {
+      uint8_t* st = smem + stage * STAGE;
+#pragma unroll
+      for (int grp = 0; grp < NGRP; ++grp) {
+        const int rb = RPW * qw + 8 * grp;
+        const int x = (rb >> 3) & 1;
+        uint8_t* base = st + rb * G::MAIN + cm_lane;
+#pragma unroll
+        for (int i = 0; i < NCI; ++i)
+          *reinterpret_cast<u32x4*>(base + 128 * (i ^ x)) = ld[grp * NCI + i];
+      }
+      if constexpr (NLDT > 0) {
+#pragma unroll
+        for (int j = 0; j < NLDT; ++j)
+          *reinterpret_cast<u32x4*>(st + off_tail(RPW * qw + TROWS * j + lane / G::TCH, lane % G::TCH)) =
+              ld[NLDM + j];
+      }
+      if (lane == 0) s_mask[stage][qw] = vm;
+    };
+
+    // slot ids of the first two tiles, then q, then the first tile's rows: all
+    // in flight together, and the q loads complete before the loop (the wait
+    // for tile 0 covers them), so the loop never waits on them
+    u32x4 ld[NLD];
+    uint32_t vm = 0;
+    int vA = load_idx(0);
+    const int vB = load_idx(1);
+
+    // ---- q operand (B of QK^T): lane (head m16, g) holds bf16 columns
+    // 32kb + 8g .. +8, or e4m3 codes of columns 128kb + 32g .. +32
+    u32x4 qf[KV8 ? 1 : G::NKB];
+    i32x8 q8[KV8 ? G::NKB : 1];
+    u32x4 qv[KV8 ? G::NKB : 1][4];
+    if constexpr (!KV8) {
+#pragma unroll
+      for (int kb = 0; kb < G::NKB; ++kb)
+        qf[kb] = *reinterpret_cast<const u32x4*>(qrow + kb * 32 + 8 * g);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int col = 128 * kb + 32 * g + 8 * jj;
+          // columns past Dqk (the last k-step of Dqk = 576) are zero; the load
+          // address is clamped so every load issues unconditionally
+          const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + min(col, DQK - 8));
+          qv[kb][jj] = (col < DQK) ? v : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    // bf16: keep every q load ahead of the row loads, so the wait for tile 0
+    // retires them and the loop never waits on them.  e4m3: the rows are
+    // requested once q is quantised (fewer registers live at once).
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!KV8) issue(ld, vm, vA);
+
+    float c2;
+    if constexpr (!KV8) {
+      c2 = p.sm_scale * p.kv_scale * kLog2e;
+    } else {
+      // the 64 heads are exactly one quantisation tile: amax over the four
+      // score waves' registers, then s_q = amax / 448 and codes in registers
+      float am = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            am = fmaxf(am, fmaxf(fabsf(bf16_lo(qv[kb][jj][i])), fabsf(bf16_hi(qv[kb][jj][i]))));
+      am = wave_max(am);
+      if (lane == 0) s_red[qw] = am;
+      __syncthreads();
+      const float amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+      const float s_q = q_scale_from_amax(amax);
+      const float r_q = 1.0f / s_q;
+      auto quantize = [&](auto fast) {
+#pragma unroll
+        for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const u32x2 c = quantize_chunk<decltype(fast)::value>(qv[kb][jj], s_q, r_q);
+            q8[kb][2 * jj] = (int)c[0];
+            q8[kb][2 * jj + 1] = (int)c[1];
+          }
+      };
+      if (q_tile_fast_div(amax)) quantize(std::true_type{});
+      else quantize(std::false_type{});
+      c2 = p.sm_scale * p.kv_scale * s_q * kLog2e;
+      issue(ld, vm, vA);
+    }
+
+    commit(0, ld, vm);                     // tile 0 -> stage 0
+    vA = load_idx(2);
+    issue(ld, vm, vB);                     // tile 1 in flight (zeros past the split)
+    __syncthreads();
+
+    // QK reads (bf16): row 16b + m16 has key m16, so chunk 4kb + g lands at
+    // 4 (kb ^ (m16 >> 2)) + (g ^ (m16 & 3)): one lane base per kb mod 4
+    int qk_base[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) qk_base[r4] = m16 * G::MAIN + 64 * (r4 ^ (m16 >> 2)) + 16 * (g ^ (m16 & 3));
+
+    float m_run = -INFINITY;   // reference max (log2 domain) of this lane's head; may lag by kSlack
+    float l_run = 0.0f;        // this lane's share of the denominator
+    int sq = 0;                // stage of tile j
+    for (int j = 0; j < nt; ++j) {
+      const int sc = (sq == 2) ? 0 : sq + 1;   // stage of tile j + 1
+      if (j + 1 < nt) commit(sc, ld, vm);
+      if (j + 2 < nt) issue(ld, vm, vA);
+      vA = load_idx(j + 3);                    // consumed a whole phase later
+
+      // ---- S^T[row][head] for the tile's NB row blocks
+      const uint8_t* st = smem + sq * STAGE;
+      f32x4 acc[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+        const int r = 16 * b + m16;
+        if constexpr (!KV8) {
+#pragma unroll
+          for (int kb = 0; kb < G::NKB; ++kb) {
+            const u32x4 a = (kb < G::MCH / 4)
+                                ? lds_read16(st + 16 * b * G::MAIN + qk_base[kb & 3] + 256 * (kb >> 2))
+                                : lds_read16(st + off_tail(r, 4 * kb + g - G::MCH));
+            a4 = mfma_bf16(a, qf[kb], a4);
+          }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < G::NKB; ++kb) {
+            const int c = 8 * kb + 2 * g;
+            u32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+            if (kb < G::MCH / 8) {
+              a0 = lds_read16(st + off_main(r, c));
+              a1 = lds_read16(st + off_main(r, c + 1));
+            } else if (2 * g < G::TCH) {   // RoPE columns; the rest of the k-step is zero
+              a0 = lds_read16(st + off_tail(r, c - G::MCH));
+              a1 = lds_read16(st + off_tail(r, c - G::MCH + 1));
+            }
+            const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                             (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            a4 = mfma_fp8(a, q8[kb], a4);
+          }
+        }
+        acc[b] = a4;
+      }
+
+      // ---- online softmax with a lazily moved reference max
+      uint64_t tm = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) tm |= (uint64_t)s_mask[sq][w] << (RPW * w);
+      float sv[NB][4];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[b][i] = ((tm >> (16 * b + 4 * g + i)) & 1ull) ? acc[b][i] * c2 : -INFINITY;
+          mt = fmaxf(mt, sv[b][i]);
+        }
+      mt = group4_max(mt);
+      int moved = 0;
+      if (__ballot(mt > m_run + kSlack) != 0) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+        if (g == 0) s_alpha[j & 1][16 * qw + m16] = alpha;
+        moved = 1;
+      }
+      if (lane == 0) s_flag[j & 1][qw] = moved;
+      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+      uint32_t pk[NB][2];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float e0 = __builtin_amdgcn_exp2f(sv[b][0] - m_use);
+        const float e1 = __builtin_amdgcn_exp2f(sv[b][1] - m_use);
+        const float e2 = __builtin_amdgcn_exp2f(sv[b][2] - m_use);
+        const float e3 = __builtin_amdgcn_exp2f(sv[b][3] - m_use);
+        l_run += (e0 + e1) + (e2 + e3);
+        pk[b][0] = pack_bf16(e0, e1);
+        pk[b][1] = pack_bf16(e2, e3);
+      }
+      // P^T operand of k-step ks, head block qw: k-slots = rows 32ks + {4g+i, 16+4g+i}
+      uint8_t* pb = pbuf + (j & 1) * PBUF;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        *reinterpret_cast<u32x4*>(pb + ((ks * 4 + qw) * 64 + lane) * 16) =
+            u32x4{pk[2 * ks][0], pk[2 * ks][1], pk[2 * ks + 1][0], pk[2 * ks + 1][1]};
+      sq = sc;
+      __syncthreads();
+    }
+
+    // ---- the output waves need the denominators; this wave writes lse
+    const float l = group4_sum(l_run);
+    if (g == 0) s_lfin[16 * qw + m16] = l;
+    __syncthreads();   // pairs with the output waves' last PV phase
+    if (g == 0) {
+      const bool any = l > 0.0f;
+      const float lse_nat = any ? (m_run + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+      const int64_t th = (int64_t)t * p.H + head;
+      if (p.S == 1) p.lse[th] = lse_nat;
+      else p.part_lse[(int64_t)s * p.T * p.H + th] = lse_nat;
+    }
+  } else {
+    // =============================== output waves ==============================
+    const int pw = wave - 4;               // output columns 128 pw .. 128 pw + 127
+    if constexpr (KV8) __syncthreads();    // q amax exchange of the score waves
+    __syncthreads();                       // tile 0 in LDS
+
+    // PV reads (bf16): row 16h + 4g + i (key 4g + i), chunk 16pw + m16 lands at
+    // 16pw + (m16 ^ (4g + i))
+    int pv_base[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv_base[i] = (4 * g + i) * G::MAIN + 16 * (16 * pw + (m16 ^ (4 * g + i)));
+
+    f32x4 O[8][4];   // [column e of the lane's 8-column chunks][head block]
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) O[e][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    __syncthreads();   // phase 0: the score waves score tile 0
+
+    // O^T[col][head] += V^T[col][row] P^T[row][head] for tile jj (stage sp)
+    auto pv = [&](int sp, int jj) {
+      const uint8_t* st = smem + sp * STAGE;
+      const uint8_t* pb = pbuf + (jj & 1) * PBUF;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        u32x4 B[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          B[hb] = *reinterpret_cast<const u32x4*>(pb + ((ks * 4 + hb) * 64 + lane) * 16);
+        u32x4 R[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 32 * ks + 16 * h + 4 * g + i;
+            if constexpr (!KV8) {
+              R[4 * h + i] = lds_read16(st + pv_base[i] + (32 * ks + 16 * h) * G::MAIN);
+            } else {
+              const int c = 16 * pw + m16;   // 8-column chunk = half of a 16-byte e4m3 chunk
+              const u32x2 raw = lds_read8(st + off_main(row, c >> 1) + 8 * (c & 1));
+              const u32x2 lo = e4m3x4_to_bf16x4(raw[0]);
+              const u32x2 hi = e4m3x4_to_bf16x4(raw[1]);
+              R[4 * h + i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+          }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int w = e >> 1;
+          u32x4 A;
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            A[x] = (e & 1) ? pack_hi(R[2 * x][w], R[2 * x + 1][w]) : pack_lo(R[2 * x][w], R[2 * x + 1][w]);
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) O[e][hb] = mfma_bf16(A, B[hb], O[e][hb]);
+        }
+      }
+    };
+
+    // Phase j multiplies tile j - 1.  The rescale of O (rare: the first valid
+    // tile, then only when a head's max outgrows the reference by 2^kSlack)
+    // sits in the outer loop, so the inner loop touches O only through MFMAs.
+    int j = 1;
+    int sp = 0;          // stage of tile j - 1
+    bool rescaled = false;
+    for (;;) {
+      for (; j <= nt; ++j) {
+        const int fb = (j - 1) & 1;
+        const int fl = __builtin_amdgcn_readfirstlane(s_flag[fb][0] | s_flag[fb][1] | s_flag[fb][2] | s_flag[fb][3]);
+        if (fl != 0 && !rescaled) break;
+        rescaled = false;
+        pv(sp, j - 1);
+        sp = (sp == 2) ? 0 : sp + 1;
+        __syncthreads();
+      }
+      if (j > nt) break;
+      const int fb = (j - 1) & 1;
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        const float a = s_flag[fb][hb] ? s_alpha[fb][16 * hb + m16] : 1.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) O[e][hb] *= a;
+      }
+      rescaled = true;
+    }
+
+    // ---- epilogue: lane (m16, g) holds columns 128pw + 32g + 8i + e of head
+    // 16hb + m16 in O[e][hb][i]
+    const int d0 = 128 * pw + 32 * g;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const float Lsum = s_lfin[16 * hb + m16];
+      const float scale = Lsum > 0.0f ? p.kv_scale / Lsum : 0.0f;
+      const int64_t th = (int64_t)t * p.H + h0 + 16 * hb + m16;
+      if (p.S == 1) {
+        u32x4* dst = reinterpret_cast<u32x4*>(p.out + th * kDV + d0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int j0 = 8 * k + 2 * x, j1 = j0 + 1;   // column offset 8i + e
+            w4[x] = pack_bf16(O[j0 & 7][hb][j0 >> 3] * scale, O[j1 & 7][hb][j1 >> 3] * scale);
+          }
+          dst[k] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+        }
+      } else {
+        f32x4* dst = reinterpret_cast<f32x4*>(p.part_o + ((int64_t)s * p.T * p.H + th) * kDV + d0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          f32x4 v;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int jx = 4 * k + x;
+            v[x] = O[jx & 7][hb][jx >> 3] * scale;
+          }
+          dst[k] = v;
+        }
+      }
+    }
+  }
+}
+
 // ---- split merge: out = sum_s w_s * O_s / sum_s w_s, w_s = exp(lse_s - max) ----
 // One (token, head) pair per 128 threads, 4 columns per thread.  The lse and
 // partial loads of up to 8 splits are issued together (an empty split's
@@ -930,7 +1356,7 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
         hipLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 16>), gd, bd, 0, stream, p);
       break;
     case 32: hipLaunchKernelGGL((smla_tiles_kernel<KV8, DQK, 32>), gd, bd, 0, stream, p); break;
-    default: hipLaunchKernelGGL((smla_tiles_kernel<KV8, DQK, 64>), gd, bd, 0, stream, p); break;
+    default: hipLaunchKernelGGL((smla_heads_kernel<KV8, DQK>), gd, dim3(2 * kThreads), 0, stream, p); break;
   }
   return hipGetLastError();
 }

@@ -66,6 +66,10 @@ MINIS = [
     (2, 128, 576, 321, 4096, "fp8", 64, 0.1),
     (1, 16, 512, 1, 64, "bf16", 64, 0.0),         # K = 1
     (7, 16, 512, 64, 256, "bf16", 64, 0.0),       # exactly one tile
+    (2, 64, 512, 190, 1024, "fp8", 64, 0.05),     # 64-head groups, e4m3
+    (3, 192, 512, 100, 2048, "bf16", 64, 0.0),    # three 64-head groups
+    (2, 64, 576, 40, 512, "bf16", 64, 0.3),       # shorter than one tile
+    (2, 128, 512, 700, 8192, "fp8", 1, 0.1),      # many tiles, block size 1
 ]
 
 
@@ -84,9 +88,10 @@ def test_mini_parity(T, H, D, K, ctx, kv, bs, pad, splits):
 
 # ---------------------------------------------------------------- gather / masking, bit-exact
 
+@pytest.mark.parametrize("H", [16, 64])
 @pytest.mark.parametrize("kv,D", [("bf16", 512), ("bf16", 576), ("fp8", 512), ("fp8", 576)])
-def test_single_index_returns_row_exactly(kv, D):
-    case = gpu_case(T=1, H=16, Dqk=D, K=64, ctx=512, kv_dtype=kv, block_size=64, seed=3)
+def test_single_index_returns_row_exactly(kv, D, H):
+    case = gpu_case(T=1, H=H, Dqk=D, K=64, ctx=512, kv_dtype=kv, block_size=64, seed=3)
     N = case.spec.N
     flat = case.kv_pool.reshape(N, D)
     for r in (0, 1, 63, 64, 65, 127, 128, 200, N - 65, N - 64, N - 1):
@@ -101,15 +106,16 @@ def test_single_index_returns_row_exactly(kv, D):
                 else:
                     want = row.view(torch.float8_e4m3fn).float() * np.float32(case.kv_scale)
                 want = want.to(torch.bfloat16)
-                want = torch.where(want == 0, torch.zeros_like(want), want).expand(16, 512)
+                want = torch.where(want == 0, torch.zeros_like(want), want).expand(H, 512)
                 assert torch.equal(out[0].view(torch.int16), want.contiguous().view(torch.int16)), (r, pos)
     # lse of the last one against the oracle
     ref_out, ref_lse = oracle_for_tokens(case, idx=idx)
     assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= 1e-3
 
 
-def test_all_padding_and_zero_k():
-    case = gpu_case(T=3, H=16, K=70, ctx=512, seed=4)
+@pytest.mark.parametrize("H", [16, 128])
+def test_all_padding_and_zero_k(H):
+    case = gpu_case(T=3, H=H, K=70, ctx=512, seed=4)
     idx = torch.full((3, 70), -1, dtype=torch.int32, device=DEV)
     for splits in (0, 1, 2):
         out, lse = run(case, idx=idx, num_splits=splits)
@@ -201,6 +207,29 @@ def test_split_invariance_and_determinism(kv):
         assert (l - base_l).abs().max().item() <= 1e-4   # fp32 summation order only
         o2, l2 = run(case, num_splits=s)
         assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(l, l2)
+
+
+@pytest.mark.parametrize("H,D", [(16, 512), (64, 576), (128, 512)])
+@pytest.mark.parametrize("growing", [True, False])
+def test_scores_that_keep_growing(H, D, growing):
+    # Every head of a token gets the same q, the scale is large (scores spread
+    # over ~+-35 nats) and each list is sorted by score: ascending, the running
+    # max rises by far more than the online softmax's rescale threshold over
+    # and over; descending, only the first tile sets it.
+    case = gpu_case(T=2, H=H, Dqk=D, K=300, ctx=4096, seed=14)
+    case.q = case.q[:, :1].expand(-1, H, -1).contiguous()
+    case.sm_scale = 8.0 / math.sqrt(D)
+    N = case.spec.N
+    flat = case.kv_pool.reshape(N, D).float().cpu()
+    idx = case.topk_idx.cpu().long()
+    q0 = case.q[:, 0].float().cpu()
+    sc = torch.einsum("tkd,td->tk", flat[idx], q0)
+    order = torch.argsort(sc, dim=1, descending=not growing)
+    idx = torch.gather(idx, 1, order).to(torch.int32).to(DEV)
+    ref_out, ref_lse = oracle_for_tokens(case, idx=idx)
+    for splits in (1, 0):
+        out, lse = run(case, num_splits=splits, idx=idx)
+        compare(out, lse, ref_out, ref_lse, "bf16", f"growing={growing} H{H} D{D} S{splits}")
 
 
 def test_kv_scale_multiplies_non_power_of_two():
