@@ -41,8 +41,18 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of the benchmark, run --steps plain device copies of BYTES "
+                         "(fp32 x * 1 into another buffer): the reference for scaling the HBM "
+                         "byte counters of rocprofv3")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("KERNEL_FETCH", "KERNEL_WRITE",
+                                                           "COPY_FETCH", "COPY_WRITE"),
+                    help="instead of the benchmark, turn four rocprofv3 --pmc output folders "
+                         "(FETCH_SIZE / WRITE_SIZE of this workload, then of --copy-calibration "
+                         "--copy-bytes) into profiles/traffic_<workload>.json")
+    ap.add_argument("--copy-bytes", type=int, default=0)
     return ap.parse_args()
 
 
@@ -95,6 +105,65 @@ def traffic_from_profiles(workload: str, launches_bytes: float):
     return rec.get("hbm_bytes_per_launch")
 
 
+def copy_calibration(nbytes: int, steps: int) -> None:
+    """A plain streaming copy of known size: its FETCH_SIZE / WRITE_SIZE per
+    dispatch give the factor from counter units to HBM bytes."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(max(steps, 1)):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
+                      "launches": max(steps, 1)}), flush=True)
+
+
+def _counter_per_dispatch(folder: str, counter: str, select):
+    """Mean over dispatches of `counter` (summed over its instances) for the
+    kernels whose name passes `select`, from a rocprofv3 --pmc csv folder."""
+    import collections
+    import csv
+    import glob
+    per = collections.defaultdict(float)
+    names = {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter or not select(row["Kernel_Name"]):
+                continue
+            per[row["Dispatch_Id"]] += float(row["Counter_Value"])
+            names[row["Dispatch_Id"]] = row["Kernel_Name"]
+    if not per:
+        raise RuntimeError(f"no {counter} rows in {folder}")
+    vals = list(per.values())
+    return sum(vals) / len(vals), len(vals), sorted(set(names.values()))
+
+
+def traffic_summary(workload: str, dirs, copy_bytes: int) -> None:
+    kf, kw, cf, cw = dirs
+    main = lambda k: "smla_" in k and "combine" not in k and "quantize" not in k
+    big = lambda k: "MulFunctor" in k           # the x * 1 copy, not the fill before it
+    fetch, n_f, names = _counter_per_dispatch(kf, "FETCH_SIZE", main)
+    write, n_w, _ = _counter_per_dispatch(kw, "WRITE_SIZE", main)
+    c_fetch, _, c_names = _counter_per_dispatch(cf, "FETCH_SIZE", big)
+    c_write, _, _ = _counter_per_dispatch(cw, "WRITE_SIZE", big)
+    f_scale = copy_bytes / c_fetch      # HBM bytes per counter unit, reads
+    w_scale = copy_bytes / c_write      # ... writes
+    rec = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+           "kernels": names, "dispatches": [n_f, n_w],
+           "fetch_size_per_dispatch": round(fetch, 1), "write_size_per_dispatch": round(write, 1),
+           "copy_kernel": c_names, "copy_bytes": copy_bytes,
+           "copy_fetch_size": round(c_fetch, 1), "copy_write_size": round(c_write, 1),
+           "read_bytes_per_unit": round(f_scale, 3), "write_bytes_per_unit": round(w_scale, 3),
+           "hbm_read_bytes_per_launch": int(fetch * f_scale),
+           "hbm_write_bytes_per_launch": int(write * w_scale),
+           "hbm_bytes_per_launch": int(fetch * f_scale + write * w_scale)}
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec), flush=True)
+
+
 def cpu_baseline(cases, budget_s: float):
     """The fp64 oracle (as it stands) on the host: whole decode calls of the same
     workload, repeated over index sets until about `budget_s` seconds."""
@@ -121,7 +190,7 @@ def cpu_baseline(cases, budget_s: float):
                        case))
         if len(staged) >= 2:
             break
-    while t_total < budget_s and n_calls < 8:
+    while t_total < budget_s and n_calls < 96:
         q, kv, remap, nbytes, case = staged[n_calls % len(staged)]
         t0 = time.perf_counter()
         oracle.sparse_mla_fwd(q, kv, remap, case.sm_scale, case.kv_scale)
@@ -138,11 +207,18 @@ def cpu_baseline(cases, budget_s: float):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(args.workload, args.traffic_summary, args.copy_bytes)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the sparse MLA "
               f"forward pass here runs on a single MI355X with no sharding or collectives.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
 
     import numpy as np
     import torch

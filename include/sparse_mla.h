@@ -68,9 +68,9 @@ typedef struct {
                                 otherwise 1..SMLA_MAX_SPLITS */
   int32_t reserved0;         /* must be zero */
   void* kernel_events[2];    /* optional instrumentation: two caller-created hipEvent_t
-                                recorded on the stream immediately before and after the
-                                main (gather + attention) kernel, not around the split
-                                combine; NULL = not recorded */
+                                that take the start and end timestamps of the main
+                                (gather + attention) kernel's own dispatch (not the split
+                                combine); NULL = not recorded */
   int32_t reserved[4];       /* must be zero */
 } smla_options_t;
 
@@ -122,9 +122,11 @@ smla_status_t sparse_mla_fwd_ex(const void* q, int64_t T, int64_t H, int64_t Dqk
                                 void* stream, const smla_options_t* opts);
 
 /*
- * Split-K factor the library picks for this shape on the current device
- * (queries its compute-unit count).  num_splits > 0 is validated and returned
- * as is.  Returns 0 on error (see sparse_mla_last_error).
+ * Split-K factor a call with these sizes runs with.  num_splits = 0: the
+ * library's choice for the current device (it queries the compute-unit count).
+ * num_splits > 0: that request, validated (<= SMLA_MAX_SPLITS) and reduced to
+ * what the top-k length allows (every split gets whole 64-entry tiles).
+ * Returns 0 on error (see sparse_mla_last_error).
  */
 int32_t sparse_mla_num_splits(int64_t T, int64_t H, int64_t K, int64_t Dqk,
                               int32_t kv_dtype, int32_t num_splits);

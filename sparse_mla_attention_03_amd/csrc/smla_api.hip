@@ -183,12 +183,8 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
             plan.S, plan.rps);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess)
-    return fail(SMLA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  e = smla::launch_fwd(p, kv_dtype == SMLA_KV_FP8_E4M3, (int)Dqk, s);
+  e = smla::launch_fwd(p, kv_dtype == SMLA_KV_FP8_E4M3, (int)Dqk, s, ev0, ev1);
   if (e != hipSuccess) return fail(SMLA_ERR_HIP, "forward kernel launch: %s", hipGetErrorString(e));
-  if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess)
-    return fail(SMLA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   if (plan.S > 1) {
     e = smla::launch_combine(p, s);
     if (e != hipSuccess) return fail(SMLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));

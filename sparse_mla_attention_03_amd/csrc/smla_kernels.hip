@@ -30,6 +30,8 @@
 //            kernel (log-sum-exp weights).
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "smla_device.h"
 #include "smla_kernels.h"
 
@@ -886,7 +888,9 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
   const int h0 = hg * 64;
   const int kbeg = s * p.rps;
   const int kend = min(kbeg + p.rps, p.K);
-  const int nt = kend > kbeg ? (kend - kbeg + TR - 1) / TR : 0;
+  // tiles, rounded up to even: the score waves run two phases per trip with
+  // no exit in between (an odd count gets one all-padding tile, which adds 0)
+  const int nt = kend > kbeg ? (((kend - kbeg + TR - 1) / TR + 1) & ~1) : 0;
   const uint16_t* qtok = p.q + (int64_t)t * p.q_st;
   uint8_t* pbuf = smem + 3 * STAGE;
 
@@ -905,14 +909,20 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     const __amdgpu_buffer_rsrc_t pool =
         __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, (short)G::ROW, (int)nrec, kBufferRsrcWord3);
 
+    // slot ids through a raw buffer over this split's entries: the load is
+    // issued for every lane (out of range reads zero), then masked to -1
+    const __amdgpu_buffer_rsrc_t ids = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(idx_t + kbeg), (short)0, (int)(4 * (kend > kbeg ? kend - kbeg : 0)), kBufferRsrcWord3);
     auto load_idx = [&](int j) -> int {
-      const int k = kbeg + TR * j + RPW * qw + (lane & (RPW - 1));
-      return (lane < RPW && k < kend) ? idx_t[k] : -1;
+      return raw_load_b32(ids, 4 * (TR * j + RPW * qw + (lane & (RPW - 1))), 0, 0);
     };
-    // rows of this wave's share of a tile: 8 rows x 128 bytes per load (lane l:
-    // row l >> 3, chunk l & 7 of a 128-byte piece); padding reads zeros
-    auto issue = [&](u32x4 (&ld)[NLD], uint32_t& vm, int vslot) {
-      const bool ok = lane < RPW && vslot >= 0 && (int64_t)vslot < p.N;
+    // rows of this wave's share of tile j: 8 rows x 128 bytes per load (lane l:
+    // row l >> 3, chunk l & 7 of a 128-byte piece); padding, entries past the
+    // split and lanes >= RPW read zeros.  The range test is made here, not at
+    // the slot id load, so nothing waits on that load before it is needed.
+    auto issue = [&](u32x4 (&ld)[NLD], uint32_t& vm, int vslot, int j) {
+      const int k = kbeg + TR * j + RPW * qw + (lane & (RPW - 1));
+      const bool ok = lane < RPW && k < kend && vslot >= 0 && (int64_t)vslot < p.N;
       vm = (uint32_t)__ballot(ok);
       const int rec = ok ? vslot : -1;
 #pragma unroll
@@ -956,10 +966,11 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     // slot ids of the first two tiles, then q, then the first tile's rows: all
     // in flight together, and the q loads complete before the loop (the wait
     // for tile 0 covers them), so the loop never waits on them
-    u32x4 ld[NLD];
-    uint32_t vm = 0;
+    u32x4 ldA[NLD], ldB[NLD];              // two tiles in flight: odd tiles in A, even in B
+    uint32_t vmA = 0, vmB = 0;
     int vA = load_idx(0);
     const int vB = load_idx(1);
+    const int vC = load_idx(2);
 
     // ---- q operand (B of QK^T): lane (head m16, g) holds bf16 columns
     // 32kb + 8g .. +8, or e4m3 codes of columns 128kb + 32g .. +32
@@ -986,7 +997,7 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     // retires them and the loop never waits on them.  e4m3: the rows are
     // requested once q is quantised (fewer registers live at once).
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!KV8) issue(ld, vm, vA);
+    if constexpr (!KV8) issue(ldA, vmA, vA, 0);
 
     float c2;
     if constexpr (!KV8) {
@@ -1021,12 +1032,18 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
       if (q_tile_fast_div(amax)) quantize(std::true_type{});
       else quantize(std::false_type{});
       c2 = p.sm_scale * p.kv_scale * s_q * kLog2e;
-      issue(ld, vm, vA);
+      issue(ldA, vmA, vA, 0);
     }
 
-    commit(0, ld, vm);                     // tile 0 -> stage 0
-    vA = load_idx(2);
-    issue(ld, vm, vB);                     // tile 1 in flight (zeros past the split)
+    commit(0, ldA, vmA);                   // tile 0 -> stage 0
+    // The order of these loads is what the loop's waits count on (set A and
+    // its ids strictly before set B and its ids); sched_barrier pins it.
+    issue(ldA, vmA, vB, 1);                // tiles 1 and 2 in flight (zeros past the split)
+    vA = load_idx(3);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(ldB, vmB, vC, 2);
+    int vD = load_idx(4);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
 
     // QK reads (bf16): row 16b + m16 has key m16, so chunk 4kb + g lands at
@@ -1037,47 +1054,91 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
 
     float m_run = -INFINITY;   // reference max (log2 domain) of this lane's head; may lag by kSlack
     float l_run = 0.0f;        // this lane's share of the denominator
-    int sq = 0;                // stage of tile j
-    for (int j = 0; j < nt; ++j) {
-      const int sc = (sq == 2) ? 0 : sq + 1;   // stage of tile j + 1
-      if (j + 1 < nt) commit(sc, ld, vm);
-      if (j + 2 < nt) issue(ld, vm, vA);
-      vA = load_idx(j + 3);                    // consumed a whole phase later
 
-      // ---- S^T[row][head] for the tile's NB row blocks
-      const uint8_t* st = smem + sq * STAGE;
-      f32x4 acc[NB];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
-        const int r = 16 * b + m16;
-        if constexpr (!KV8) {
-#pragma unroll
-          for (int kb = 0; kb < G::NKB; ++kb) {
-            const u32x4 a = (kb < G::MCH / 4)
-                                ? lds_read16(st + 16 * b * G::MAIN + qk_base[kb & 3] + 256 * (kb >> 2))
-                                : lds_read16(st + off_tail(r, 4 * kb + g - G::MCH));
-            a4 = mfma_bf16(a, qf[kb], a4);
-          }
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < G::NKB; ++kb) {
-            const int c = 8 * kb + 2 * g;
-            u32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-            if (kb < G::MCH / 8) {
-              a0 = lds_read16(st + off_main(r, c));
-              a1 = lds_read16(st + off_main(r, c + 1));
-            } else if (2 * g < G::TCH) {   // RoPE columns; the rest of the k-step is zero
-              a0 = lds_read16(st + off_tail(r, c - G::MCH));
-              a1 = lds_read16(st + off_tail(r, c - G::MCH + 1));
-            }
-            const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                             (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-            a4 = mfma_fp8(a, q8[kb], a4);
-          }
+    // One QK^T A fragment: rows 16b .. 16b + 15 of the tile, bf16 columns
+    // 32kb + 8g .. +8 (one 16-byte read) or e4m3 columns 128kb + 32g .. +32
+    // (two reads; zeros past Dqk)
+    using Frag = std::conditional_t<KV8, i32x8, u32x4>;
+    auto frag = [&](const uint8_t* st, int b, int kb) -> Frag {
+      const int r = 16 * b + m16;
+      if constexpr (!KV8) {
+        return (kb < G::MCH / 4) ? lds_read16(st + 16 * b * G::MAIN + qk_base[kb & 3] + 256 * (kb >> 2))
+                                 : lds_read16(st + off_tail(r, 4 * kb + g - G::MCH));
+      } else {
+        const int c = 8 * kb + 2 * g;
+        u32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+        if (kb < G::MCH / 8) {
+          a0 = lds_read16(st + off_main(r, c));
+          a1 = lds_read16(st + off_main(r, c + 1));
+        } else if (2 * g < G::TCH) {   // RoPE columns; the rest of the k-step is zero
+          a0 = lds_read16(st + off_tail(r, c - G::MCH));
+          a1 = lds_read16(st + off_tail(r, c - G::MCH + 1));
         }
-        acc[b] = a4;
+        return i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                     (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
       }
+    };
+    // S^T[row][head] of the tile's NB row blocks.  bf16: fragments are read
+    // DEPTH k-steps ahead of their MFMA (LDS latency) and each block keeps two
+    // partial sums (even / odd k-steps), so back-to-back MFMAs are
+    // independent.  e4m3: the four blocks already are.
+    constexpr int DEPTH = 3;
+    constexpr int NACC = 2;
+    auto qk = [&](const uint8_t* st, f32x4 (&acc)[NB]) {
+      if constexpr (KV8) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[b] = mfma_fp8(frag(st, b, kb), q8[kb], acc[b]);
+      } else {
+        f32x4 ac[NB][NACC];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int h = 0; h < NACC; ++h) ac[b][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Frag ring[DEPTH][NB];
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) ring[d][b] = frag(st, b, d);
+#pragma unroll
+        for (int kb = 0; kb < G::NKB; ++kb) {
+          Frag cur[NB];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) cur[b] = ring[kb % DEPTH][b];
+          if (kb + DEPTH < G::NKB) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) ring[kb % DEPTH][b] = frag(st, b, kb + DEPTH);
+          }
+#pragma unroll
+          for (int b = 0; b < NB; ++b) ac[b][kb % NACC] = mfma_bf16(cur[b], qf[kb], ac[b][kb % NACC]);
+        }
+        // issue order: DEPTH k-steps of reads, then one MFMA per read, so
+        // NB * DEPTH reads stay in flight (the default schedule keeps ~2)
+        constexpr int NR = NB * G::NKB, PRE = NB * DEPTH;
+        __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
+#pragma unroll
+        for (int i = 0; i < NR - PRE; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          acc[b] = ac[b][0];
+#pragma unroll
+          for (int h = 1; h < NACC; ++h) acc[b] += ac[b][h];
+        }
+      }
+    };
+
+    // scores, softmax and P of the tile in stage sq, into P buffer PB
+    auto score_tile = [&](int sq, auto pb_sel) {
+      constexpr int PB = decltype(pb_sel)::value;
+      f32x4 acc[NB];
+      qk(smem + sq * STAGE, acc);
 
       // ---- online softmax with a lazily moved reference max
       uint64_t tm = 0;
@@ -1099,10 +1160,10 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
         const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
-        if (g == 0) s_alpha[j & 1][16 * qw + m16] = alpha;
+        if (g == 0) s_alpha[PB][16 * qw + m16] = alpha;
         moved = 1;
       }
-      if (lane == 0) s_flag[j & 1][qw] = moved;
+      if (lane == 0) s_flag[PB][qw] = moved;
       const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
       uint32_t pk[NB][2];
 #pragma unroll
@@ -1116,11 +1177,34 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
         pk[b][1] = pack_bf16(e2, e3);
       }
       // P^T operand of k-step ks, head block qw: k-slots = rows 32ks + {4g+i, 16+4g+i}
-      uint8_t* pb = pbuf + (j & 1) * PBUF;
+      uint8_t* pb = pbuf + PB * PBUF;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         *reinterpret_cast<u32x4*>(pb + ((ks * 4 + qw) * 64 + lane) * 16) =
             u32x4{pk[2 * ks][0], pk[2 * ks][1], pk[2 * ks + 1][0], pk[2 * ks + 1][1]};
+    };
+
+    // Two phases per trip, so each register set has fixed code: tile j + 1
+    // goes to LDS and tile j + 3 takes its registers.  Loads and commits are
+    // unconditional (past the split they read zeros into a free stage), and
+    // each set's slot ids are fetched right after its rows, a trip ahead: so
+    // no wait for one set or its ids ever covers the other set's loads.
+    int sq = 0;                // stage of tile j
+    for (int j = 0; j < nt; j += 2) {
+      int sc = (sq == 2) ? 0 : sq + 1;
+      commit(sc, ldA, vmA);                  // tile j + 1
+      issue(ldA, vmA, vA, j + 3);
+      vA = load_idx(j + 5);
+      __builtin_amdgcn_sched_barrier(0);
+      score_tile(sq, std::integral_constant<int, 0>{});
+      sq = sc;
+      __syncthreads();
+      sc = (sq == 2) ? 0 : sq + 1;
+      commit(sc, ldB, vmB);                  // tile j + 2
+      issue(ldB, vmB, vD, j + 4);
+      vD = load_idx(j + 6);
+      __builtin_amdgcn_sched_barrier(0);
+      score_tile(sq, std::integral_constant<int, 1>{});
       sq = sc;
       __syncthreads();
     }
@@ -1340,30 +1424,38 @@ __global__ __launch_bounds__(kThreads) void smla_quantize_q_kernel(const uint16_
 
 // ---- launch wrappers ----------------------------------------------------------------
 template <bool KV8, int DQK>
-static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
+static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const int HT = heads_per_workgroup(p.H);
   const int HG = p.H / HT;
   const int64_t units = (int64_t)p.T * p.S;
   const int64_t grid = ((units + 7) / 8) * 8 * HG;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 gd((unsigned)grid), bd(kThreads);
+  // hipExtLaunchKernelGGL: the optional events take the kernel's own start and
+  // end timestamps (no marker packets around it)
   switch (HT) {
     case 16:
       // 32-row wave tiles where four of them plus q fit in LDS, else 16
       if constexpr (KV8 || DQK == 512)
-        hipLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 32>), gd, bd, 0, stream, p);
+        hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 32>), gd, bd, 0, stream, ev0, ev1, 0, p);
       else
-        hipLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 16>), gd, bd, 0, stream, p);
+        hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 16>), gd, bd, 0, stream, ev0, ev1, 0, p);
       break;
-    case 32: hipLaunchKernelGGL((smla_tiles_kernel<KV8, DQK, 32>), gd, bd, 0, stream, p); break;
-    default: hipLaunchKernelGGL((smla_heads_kernel<KV8, DQK>), gd, dim3(2 * kThreads), 0, stream, p); break;
+    case 32:
+      hipExtLaunchKernelGGL((smla_tiles_kernel<KV8, DQK, 32>), gd, bd, 0, stream, ev0, ev1, 0, p);
+      break;
+    default:
+      hipExtLaunchKernelGGL((smla_heads_kernel<KV8, DQK>), gd, dim3(2 * kThreads), 0, stream, ev0, ev1, 0, p);
+      break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdParams& p, bool kv_fp8, int dqk, hipStream_t stream) {
-  if (kv_fp8) return dqk == 576 ? launch_fwd_t<true, 576>(p, stream) : launch_fwd_t<true, 512>(p, stream);
-  return dqk == 576 ? launch_fwd_t<false, 576>(p, stream) : launch_fwd_t<false, 512>(p, stream);
+hipError_t launch_fwd(const FwdParams& p, bool kv_fp8, int dqk, hipStream_t stream, hipEvent_t ev0,
+                      hipEvent_t ev1) {
+  if (kv_fp8)
+    return dqk == 576 ? launch_fwd_t<true, 576>(p, stream, ev0, ev1) : launch_fwd_t<true, 512>(p, stream, ev0, ev1);
+  return dqk == 576 ? launch_fwd_t<false, 576>(p, stream, ev0, ev1) : launch_fwd_t<false, 512>(p, stream, ev0, ev1);
 }
 
 hipError_t launch_combine(const FwdParams& p, hipStream_t stream) {
