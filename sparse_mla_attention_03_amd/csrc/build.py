@@ -23,6 +23,10 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: with AGPR accumulators the register allocator
+    # shuffles them between AGPR tuples every loop trip; in VGPR form the
+    # accumulators stay in place and the row prefetch buffers go to AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", HERE,
 ]

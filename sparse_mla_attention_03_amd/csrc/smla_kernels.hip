@@ -639,50 +639,108 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   float m_run = -INFINITY;
   float l_run = 0.0f;
 
-  auto compute = [&](uint32_t vm) {
-    // QK^T: S^T[row][head] per 16-row block b, lane (head = m16, g) receives
-    // rows 16b + 4g .. 16b + 4g + 3
-    f32x4 acc[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const uint8_t* blk = slot + 16 * b * G::MAIN;
-      f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (!KV8) {
-#pragma unroll
-        for (int kb = 0; kb < G::NKB; ++kb) {
-          const u32x4 a = (kb < G::MCH / 4)
-                              ? lds_read16(blk + qk_base[kb & 3] + 256 * (kb >> 2))
-                              : lds_read16(slot + off_tail(16 * b + m16, 4 * kb + g - G::MCH));
-          a4 = mfma_bf16(a, lds_read16(qlane + (kb * 32 + 8 * g) * 2), a4);
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < G::NKB; ++kb) {
-          const int c = 8 * kb + 2 * g;
-          u32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0}, b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
-          if (kb < G::MCH / 8) {
-            a0 = lds_read16(slot + off_main(16 * b + m16, c));
-            a1 = lds_read16(slot + off_main(16 * b + m16, c + 1));
-            b0 = lds_read16(qlane + 16 * c);
-            b1 = lds_read16(qlane + 16 * c + 16);
-          } else if (2 * g < G::TCH) {
-            a0 = lds_read16(slot + off_tail(16 * b + m16, c - G::MCH));
-            a1 = lds_read16(slot + off_tail(16 * b + m16, c - G::MCH + 1));
-            b0 = lds_read16(qlane + 16 * c);
-            b1 = lds_read16(qlane + 16 * c + 16);
-          }
-          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          const i32x8 bq = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
-                            (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
-          a4 = mfma_fp8(a, bq, a4);
-        }
+  // ---- QK^T of the wave's tile: S^T[row][head] per 16-row block b, lane
+  // (head = m16, g) receives rows 16b + 4g .. 16b + 4g + 3.  k-step outer,
+  // blocks inner, so each q fragment feeds NB MFMAs; two partial sums per
+  // block (even / odd k-steps) keep back-to-back MFMAs independent, and the
+  // fragments of the next DEPTH k-steps are read ahead of their MFMAs.
+  using KFrag = std::conditional_t<KV8, i32x8, u32x4>;
+  auto kfrag = [&](int b, int kb) -> KFrag {
+    if constexpr (!KV8) {
+      return (kb < G::MCH / 4) ? lds_read16(slot + 16 * b * G::MAIN + qk_base[kb & 3] + 256 * (kb >> 2))
+                               : lds_read16(slot + off_tail(16 * b + m16, 4 * kb + g - G::MCH));
+    } else {
+      const int c = 8 * kb + 2 * g;
+      u32x4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+      if (kb < G::MCH / 8) {
+        a0 = lds_read16(slot + off_main(16 * b + m16, c));
+        a1 = lds_read16(slot + off_main(16 * b + m16, c + 1));
+      } else if (2 * g < G::TCH) {   // RoPE columns; the rest of the k-step is zero
+        a0 = lds_read16(slot + off_tail(16 * b + m16, c - G::MCH));
+        a1 = lds_read16(slot + off_tail(16 * b + m16, c - G::MCH + 1));
       }
-      acc[b] = a4;
+      return i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
     }
-    // online softmax over the tile's rows
-    float sv[NB][4];
-    float mt = -INFINITY;
+  };
+  auto qfrag = [&](int kb) -> KFrag {
+    if constexpr (!KV8) {
+      return lds_read16(qlane + (kb * 32 + 8 * g) * 2);
+    } else {
+      const int c = 8 * kb + 2 * g;
+      u32x4 b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
+      if (kb < G::MCH / 8 || 2 * g < G::TCH) {
+        b0 = lds_read16(qlane + 16 * c);
+        b1 = lds_read16(qlane + 16 * c + 16);
+      }
+      return i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                   (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    }
+  };
+  constexpr int DEPTH = 2;
+  auto qk = [&](f32x4 (&acc)[NB]) {
+    if constexpr (KV8) {
+      // e4m3: few, wide k-steps (128 columns); the NB blocks are the
+      // independent chains
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < G::NKB; ++kb) {
+        const KFrag bq = qfrag(kb);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] = mfma_fp8(kfrag(b, kb), bq, acc[b]);
+      }
+      return;
+    }
+    f32x4 ac[NB][2];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) ac[b][0] = ac[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    KFrag ra[DEPTH][NB], rq[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      rq[d] = qfrag(d);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) ra[d][b] = kfrag(b, d);
+    }
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb) {
+      const KFrag bq = rq[kb % DEPTH];
+      KFrag a[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) a[b] = ra[kb % DEPTH][b];
+      if (kb + DEPTH < G::NKB) {
+        rq[kb % DEPTH] = qfrag(kb + DEPTH);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) ra[kb % DEPTH][b] = kfrag(b, kb + DEPTH);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if constexpr (!KV8) ac[b][kb & 1] = mfma_bf16(a[b], bq, ac[b][kb & 1]);
+        else ac[b][kb & 1] = mfma_fp8(a[b], bq, ac[b][kb & 1]);
+      }
+    }
+    if constexpr (!KV8) {
+      // issue order: DEPTH k-steps of reads, then per k-step NB MFMAs and the
+      // NB + 1 reads of k-step kb + DEPTH
+      constexpr int RPK = NB + 1;
+      __builtin_amdgcn_sched_group_barrier(0x100, DEPTH * RPK, 0);
+#pragma unroll
+      for (int kb = 0; kb < G::NKB; ++kb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+        if (kb + DEPTH < G::NKB) __builtin_amdgcn_sched_group_barrier(0x100, RPK, 0);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = ac[b][0] + ac[b][1];
+  };
+
+  // ---- scores of the tile in log2 units (masked rows -inf) and their max
+  float sv[NB][4];
+  float mt = -INFINITY;
+  auto score = [&](uint32_t vm) {
+    f32x4 acc[NB];
+    qk(acc);
+    mt = -INFINITY;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -691,19 +749,12 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
         mt = fmaxf(mt, sv[b][i]);
       }
     mt = group4_max(mt);
-    // m_run is a reference max that may lag the true one by up to kSlack, so
-    // exponents stay <= 2^kSlack and O is rescaled only when some head's
-    // scores outgrow it (after the first valid tile, rarely)
-    if (__ballot(mt > m_run + kSlack) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) O[a][e] *= alpha;
-    }
+  };
+
+  // ---- P = exp2(s - m_run) and O^T[dim][head] += V^T[dim][row] P^T[row][head];
+  // k-slot g holds rows 16b + 4g + i for every block b (i = 0..3), in the same
+  // order on both sides
+  auto accumulate = [&]() {
     const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
     uint32_t pk[NB][2];
 #pragma unroll
@@ -716,8 +767,6 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
       pk[b][0] = pack_bf16(e0, e1);
       pk[b][1] = pack_bf16(e2, e3);
     }
-    // PV: O^T[dim][head] += V^T[dim][row] P^T[row][head]; k-slot g holds rows
-    // 16b + 4g + i for every block b (i = 0..3), in the same order on both sides
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int c = m16 + 16 * a;   // 8-column chunk of this lane
@@ -757,14 +806,37 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   };
 
   // ---- main loop: one tile in flight in registers while the previous one
-  // computes from LDS; slot ids run two tiles ahead of the loads that use them
-  for (int i = 0; i < nt; ++i) {
-    commit(ldA);
-    const uint32_t va = vmA;
-    const int vidx_after = load_idx(i + 2);
-    if (i + 1 < nt) issue(ldA, vmA, vidx_next);   // none past the end: the merge barrier would wait for it
-    vidx_next = vidx_after;
-    compute(va);
+  // computes from LDS; slot ids run two tiles ahead of the loads that use them.
+  // m_run is a reference max that may lag the true one by up to kSlack, so
+  // exponents stay <= 2^kSlack.  A head with no valid entry yet simply takes
+  // the tile's max (its O is still zero).  Only when a head's scores outgrow a
+  // finite reference must O be rescaled; that leaves the inner loop for the
+  // outer one, so the inner loop touches O by MFMAs alone.
+  int i = 0;
+  for (;;) {
+    for (; i < nt; ++i) {
+      commit(ldA);
+      const uint32_t va = vmA;
+      const int vidx_after = load_idx(i + 2);
+      if (i + 1 < nt) issue(ldA, vmA, vidx_next);   // none past the end: the merge barrier would wait for it
+      vidx_next = vidx_after;
+      score(va);
+      if (__ballot(m_run != -INFINITY && mt > m_run + kSlack) != 0) break;
+      m_run = (m_run == -INFINITY) ? mt : m_run;
+      accumulate();
+    }
+    if (i >= nt) break;
+    // tile i is scored and outgrows a reference: rescale, accumulate, go on
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) O[a][e] *= alpha;
+    accumulate();
+    ++i;
   }
 
   // ---- merge the four waves: each writes its raw O (straight from the
