@@ -448,6 +448,14 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
 
 constexpr float kSlack = 8.0f;   // log2 headroom of the lazily rescaled running max
 
+// Swizzle key of a tile row: the 16-byte chunk c of row r sits at chunk
+// position c ^ row_key(r).  row_key is a bijection on r mod 16 (so 16
+// consecutive rows read at one chunk, and one row read across 16 chunks, hit
+// 16 different chunk positions) and rows 2j, 2j + 1 differ in bit 3 of it, so
+// the two rows a 16-lane quarter of a commit store writes side by side fall in
+// different halves of the bank space.
+__device__ __forceinline__ int row_key(int r) { return ((r & 1) << 3) | ((r >> 1) & 7); }
+
 template <bool KV8, int DQK, int TR>
 __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   using G = Geom<KV8, DQK>;
@@ -503,9 +511,9 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
       __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, (short)G::ROW, (int)nrec, kBufferRsrcWord3);
 
   uint8_t* slot = smem + wave * WSLOT;   // this wave's tile, rows 0 .. TR-1
-  // 16-byte chunk c of tile row r sits at chunk position c ^ (r & 15) (V part)
-  // or c ^ (r & (TCH-1)) (RoPE part): conflict-free row and column accesses.
-  auto off_main = [](int r, int c) { return r * G::MAIN + 16 * (c ^ (r & 15)); };
+  // 16-byte chunk c of tile row r sits at chunk position c ^ row_key(r) (V
+  // part) or c ^ (r & (TCH-1)) (RoPE part): conflict-free row and column accesses.
+  auto off_main = [](int r, int c) { return r * G::MAIN + 16 * (c ^ row_key(r)); };
   auto off_tail = [](int r, int c) { return WMAIN + r * G::TAIL + 16 * (c ^ (r & (G::TCH - 1))); };
 
   // ---- slot ids of a tile: lane j < TR holds entry k0 + j of the list, or -1
@@ -537,15 +545,24 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
     }
   };
 
-  // lane bases of the commit: row (l>>3) of a group, chunk (l&7) + 8i lands at
-  // position ((l&7) ^ (l>>3)) + 8 (i ^ (grp&1)), because row & 15 = 8 (grp&1) + (l>>3)
-  const int cm_base = (lane >> 3) * G::MAIN + 16 * ((lane & 7) ^ (lane >> 3));
+  // lane bases of the commit: lane l writes row 8grp + h (h = l >> 3), whose
+  // key is 8 (h & 1) + 4 (grp & 1) + (h >> 1), so chunk (l & 7) + 8i lands at
+  // 8 (i ^ (h & 1)) + ((l & 7) ^ (4 (grp & 1) + (h >> 1))): one base per
+  // parity of grp and of i
+  int cm_base[2][2];
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+    for (int ip = 0; ip < 2; ++ip) {
+      const int h = lane >> 3;
+      cm_base[gp][ip] = h * G::MAIN + 128 * (ip ^ (h & 1)) + 16 * ((lane & 7) ^ (4 * gp + (h >> 1)));
+    }
   auto commit = [&](const u32x4 (&ld)[NLD]) {
 #pragma unroll
     for (int grp = 0; grp < NGRP; ++grp)
 #pragma unroll
       for (int i = 0; i < NCI; ++i)
-        *reinterpret_cast<u32x4*>(slot + cm_base + 8 * grp * G::MAIN + 128 * (i ^ (grp & 1))) =
+        *reinterpret_cast<u32x4*>(slot + cm_base[grp & 1][i & 1] + 8 * grp * G::MAIN + 256 * (i >> 1)) =
             ld[grp * NCI + i];
     if constexpr (NLDT > 0) {
 #pragma unroll
@@ -621,15 +638,19 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   // lane (head = m16, g): bf16 columns 32kb + 8g .. +8, or e4m3 columns 128kb + 32g .. +32
   const uint8_t* qlane = qs + m16 * QROW;
 
-  // QK reads: row 16b + m16 (row & 15 = m16), chunk 4kb + g lands at
-  // 4 (kb ^ (m16>>2)) + (g ^ (m16&3)): four lane bases, one per kb mod 4
+  // QK reads: row 16b + m16 has key k = row_key(m16), so chunk 4kb + g lands
+  // at 4 (kb ^ (k >> 2)) + (g ^ (k & 3)): four lane bases, one per kb mod 4
   int qk_base[4];
 #pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4) qk_base[r4] = m16 * G::MAIN + 64 * (r4 ^ (m16 >> 2)) + 16 * (g ^ (m16 & 3));
-  // PV reads (bf16): row 16b + 4g + i, chunk m16 + 16a lands at 16a + (m16 ^ (4g + i))
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const int k = row_key(m16);
+    qk_base[r4] = m16 * G::MAIN + 64 * (r4 ^ (k >> 2)) + 16 * (g ^ (k & 3));
+  }
+  // PV reads (bf16): row 16b + 4g + i, chunk m16 + 16a lands at
+  // 16a + (m16 ^ row_key(4g + i))
   int pv_base[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pv_base[i] = (4 * g + i) * G::MAIN + 16 * (m16 ^ (4 * g + i));
+  for (int i = 0; i < 4; ++i) pv_base[i] = (4 * g + i) * G::MAIN + 16 * (m16 ^ row_key(4 * g + i));
 
   f32x4 O[4][8];
 #pragma unroll
@@ -966,9 +987,9 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
   const uint16_t* qtok = p.q + (int64_t)t * p.q_st;
   uint8_t* pbuf = smem + 3 * STAGE;
 
-  // 16-byte chunk c of tile row r sits at chunk position c ^ (r & 15) (V part)
-  // or c ^ (r & (TCH-1)) (RoPE part)
-  auto off_main = [](int r, int c) { return r * G::MAIN + 16 * (c ^ (r & 15)); };
+  // 16-byte chunk c of tile row r sits at chunk position c ^ row_key(r) (V
+  // part) or c ^ (r & (TCH-1)) (RoPE part)
+  auto off_main = [](int r, int c) { return r * G::MAIN + 16 * (c ^ row_key(r)); };
   auto off_tail = [](int r, int c) { return TMAIN + r * G::TAIL + 16 * (c ^ (r & (G::TCH - 1))); };
 
   if (wave < 4) {
@@ -1012,19 +1033,21 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
         }
       }
     };
-    // row rb + (l >> 3) has key 8x + (l >> 3), x = (rb >> 3) & 1, so chunk
-    // (l & 7) + 8i lands at ((l & 7) ^ (l >> 3)) + 8 (i ^ x)
-    const int cm_lane = (lane >> 3) * G::MAIN + 16 * ((lane & 7) ^ (lane >> 3));
+    // row rb + h (h = l >> 3, rb a multiple of 8) has key 8 (h & 1) + 4x +
+    // (h >> 1), x = (rb >> 3) & 1, so chunk (l & 7) + 8i lands at
+    // 8 (i ^ (h & 1)) + ((l & 7) ^ (4x + (h >> 1)))
+    const int hl = lane >> 3;
+    const int cm_par[2] = {128 * (hl & 1), -128 * (hl & 1)};   // 128 (i ^ (h&1)) - 128 i, by i parity
     auto commit = [&](int stage, const u32x4 (&ld)[NLD], uint32_t vm) {
       uint8_t* st = smem + stage * STAGE;
 #pragma unroll
       for (int grp = 0; grp < NGRP; ++grp) {
         const int rb = RPW * qw + 8 * grp;
         const int x = (rb >> 3) & 1;
-        uint8_t* base = st + rb * G::MAIN + cm_lane;
+        uint8_t* base = st + (rb + hl) * G::MAIN + 16 * ((lane & 7) ^ (4 * x + (hl >> 1)));
 #pragma unroll
         for (int i = 0; i < NCI; ++i)
-          *reinterpret_cast<u32x4*>(base + 128 * (i ^ x)) = ld[grp * NCI + i];
+          *reinterpret_cast<u32x4*>(base + 128 * i + cm_par[i & 1]) = ld[grp * NCI + i];
       }
       if constexpr (NLDT > 0) {
 #pragma unroll
@@ -1118,11 +1141,14 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
 
-    // QK reads (bf16): row 16b + m16 has key m16, so chunk 4kb + g lands at
-    // 4 (kb ^ (m16 >> 2)) + (g ^ (m16 & 3)): one lane base per kb mod 4
+    // QK reads (bf16): row 16b + m16 has key k = row_key(m16), so chunk
+    // 4kb + g lands at 4 (kb ^ (k >> 2)) + (g ^ (k & 3)): one lane base per kb mod 4
     int qk_base[4];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) qk_base[r4] = m16 * G::MAIN + 64 * (r4 ^ (m16 >> 2)) + 16 * (g ^ (m16 & 3));
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int k = row_key(m16);
+      qk_base[r4] = m16 * G::MAIN + 64 * (r4 ^ (k >> 2)) + 16 * (g ^ (k & 3));
+    }
 
     float m_run = -INFINITY;   // reference max (log2 domain) of this lane's head; may lag by kSlack
     float l_run = 0.0f;        // this lane's share of the denominator
@@ -1298,11 +1324,11 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     if constexpr (KV8) __syncthreads();    // q amax exchange of the score waves
     __syncthreads();                       // tile 0 in LDS
 
-    // PV reads (bf16): row 16h + 4g + i (key 4g + i), chunk 16pw + m16 lands at
-    // 16pw + (m16 ^ (4g + i))
+    // PV reads (bf16): row 16h + 4g + i (key row_key(4g + i)), chunk 16pw + m16
+    // lands at 16pw + (m16 ^ row_key(4g + i))
     int pv_base[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pv_base[i] = (4 * g + i) * G::MAIN + 16 * (16 * pw + (m16 ^ (4 * g + i)));
+    for (int i = 0; i < 4; ++i) pv_base[i] = (4 * g + i) * G::MAIN + 16 * (16 * pw + (m16 ^ row_key(4 * g + i)));
 
     f32x4 O[8][4];   // [column e of the lane's 8-column chunks][head block]
 #pragma unroll
