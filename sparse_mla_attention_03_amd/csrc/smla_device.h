@@ -97,14 +97,24 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// max / sum over the four lanes l, l^16, l^32, l^48 (the k-slot groups)
+// max / sum over the four lanes l, l^16, l^32, l^48 (the k-slot groups),
+// with the gfx950 lane swaps instead of LDS permutes: permlane32_swap(v, v)
+// yields {v[l mod 32], v[l mod 32 + 32]} and permlane16_swap(v, v) the same
+// for 16-lane rows, so each step pairs lane l with l^32, then with l^16.
+__device__ __forceinline__ float xor32_op_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float group4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  v = xor32_op_max(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float group4_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // ---- per-tile q quantisation (fp8 dots) ---------------------------------------

@@ -1235,13 +1235,13 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     // scores, softmax and P of the tile in stage sq, into P buffer PB
     auto score_tile = [&](int sq, auto pb_sel) {
       constexpr int PB = decltype(pb_sel)::value;
+      uint64_t tm = 0;   // validity of the tile's rows (read before the MFMAs)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) tm |= (uint64_t)s_mask[sq][w] << (RPW * w);
       f32x4 acc[NB];
       qk(smem + sq * STAGE, acc);
 
       // ---- online softmax with a lazily moved reference max
-      uint64_t tm = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) tm |= (uint64_t)s_mask[sq][w] << (RPW * w);
       float sv[NB][4];
       float mt = -INFINITY;
 #pragma unroll
@@ -1290,19 +1290,21 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     int sq = 0;                // stage of tile j
     for (int j = 0; j < nt; j += 2) {
       int sc = (sq == 2) ? 0 : sq + 1;
-      commit(sc, ldA, vmA);                  // tile j + 1
+      score_tile(sq, std::integral_constant<int, 0>{});
+      __builtin_amdgcn_sched_barrier(0);
+      commit(sc, ldA, vmA);                  // tile j + 1, after the MFMAs are under way
       issue(ldA, vmA, vA, j + 3);
       vA = load_idx(j + 5);
       __builtin_amdgcn_sched_barrier(0);
-      score_tile(sq, std::integral_constant<int, 0>{});
       sq = sc;
       __syncthreads();
       sc = (sq == 2) ? 0 : sq + 1;
+      score_tile(sq, std::integral_constant<int, 1>{});
+      __builtin_amdgcn_sched_barrier(0);
       commit(sc, ldB, vmB);                  // tile j + 2
       issue(ldB, vmB, vD, j + 4);
       vD = load_idx(j + 6);
       __builtin_amdgcn_sched_barrier(0);
-      score_tile(sq, std::integral_constant<int, 1>{});
       sq = sc;
       __syncthreads();
     }
@@ -1338,9 +1340,30 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
 
     __syncthreads();   // phase 0: the score waves score tile 0
 
-    // O^T[col][head] += V^T[col][row] P^T[row][head] for tile jj (stage sp)
-    auto pv = [&](int sp, int jj) {
+    // V fragments of a tile (rows 32ks + {4g + i, 16 + 4g + i}, the lane's 8
+    // columns 8 (16pw + m16) ..), read one phase ahead of their MFMAs: tile j
+    // is in LDS from the start of phase j, its PV runs in phase j + 1
+    u32x4 Rv[NKS][8];
+    auto pv_load = [&](int sp) {
       const uint8_t* st = smem + sp * STAGE;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 32 * ks + 16 * h + 4 * g + i;
+            if constexpr (!KV8) {
+              Rv[ks][4 * h + i] = lds_read16(st + pv_base[i] + (32 * ks + 16 * h) * G::MAIN);
+            } else {
+              const int c = 16 * pw + m16;   // 8-column chunk = half of a 16-byte e4m3 chunk
+              const u32x2 raw = lds_read8(st + off_main(row, c >> 1) + 8 * (c & 1));
+              Rv[ks][4 * h + i] = u32x4{raw[0], raw[1], 0u, 0u};
+            }
+          }
+    };
+    // O^T[col][head] += V^T[col][row] P^T[row][head] for tile jj from Rv
+    auto pv = [&](int jj) {
       const uint8_t* pb = pbuf + (jj & 1) * PBUF;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -1350,20 +1373,15 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
           B[hb] = *reinterpret_cast<const u32x4*>(pb + ((ks * 4 + hb) * 64 + lane) * 16);
         u32x4 R[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 32 * ks + 16 * h + 4 * g + i;
-            if constexpr (!KV8) {
-              R[4 * h + i] = lds_read16(st + pv_base[i] + (32 * ks + 16 * h) * G::MAIN);
-            } else {
-              const int c = 16 * pw + m16;   // 8-column chunk = half of a 16-byte e4m3 chunk
-              const u32x2 raw = lds_read8(st + off_main(row, c >> 1) + 8 * (c & 1));
-              const u32x2 lo = e4m3x4_to_bf16x4(raw[0]);
-              const u32x2 hi = e4m3x4_to_bf16x4(raw[1]);
-              R[4 * h + i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-            }
+        for (int r = 0; r < 8; ++r) {
+          if constexpr (!KV8) {
+            R[r] = Rv[ks][r];
+          } else {   // e4m3 -> bf16, exact
+            const u32x2 lo = e4m3x4_to_bf16x4(Rv[ks][r][0]);
+            const u32x2 hi = e4m3x4_to_bf16x4(Rv[ks][r][1]);
+            R[r] = u32x4{lo[0], lo[1], hi[0], hi[1]};
           }
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int w = e >> 1;
@@ -1380,6 +1398,7 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     // Phase j multiplies tile j - 1.  The rescale of O (rare: the first valid
     // tile, then only when a head's max outgrows the reference by 2^kSlack)
     // sits in the outer loop, so the inner loop touches O only through MFMAs.
+    pv_load(0);
     int j = 1;
     int sp = 0;          // stage of tile j - 1
     bool rescaled = false;
@@ -1389,8 +1408,9 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
         const int fl = __builtin_amdgcn_readfirstlane(s_flag[fb][0] | s_flag[fb][1] | s_flag[fb][2] | s_flag[fb][3]);
         if (fl != 0 && !rescaled) break;
         rescaled = false;
-        pv(sp, j - 1);
+        pv(j - 1);
         sp = (sp == 2) ? 0 : sp + 1;
+        pv_load(sp);     // tile j (past the last tile: a stale stage, never used)
         __syncthreads();
       }
       if (j > nt) break;
