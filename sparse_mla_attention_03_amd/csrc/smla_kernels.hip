@@ -571,8 +571,12 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
     }
   };
 
-  // ---- the group's 16 q rows: every thread loads its chunks at once (indices
-  // clamped instead of guarded, so all loads are in flight together)
+  // ---- slot ids of the first two tiles, then the group's 16 q rows (every
+  // thread loads its chunks at once; indices clamped instead of guarded, so all
+  // loads are in flight together), then the first tile's rows: the row
+  // requests wait only for the ids, and the q staging below overlaps them
+  int vidx_next = load_idx(0);
+  int vidx_next2 = load_idx(1);
   constexpr int CPR = DQK / 8;                              // 16-byte chunks per head row
   constexpr int NQ = (16 * CPR + kThreads - 1) / kThreads;  // chunks per thread
   u32x4 qv[NQ];
@@ -581,12 +585,9 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
     const int c = min(tid + r * kThreads, 16 * CPR - 1), hh = c / CPR, cc = c - hh * CPR;
     qv[r] = *reinterpret_cast<const u32x4*>(qtok + (int64_t)(h0 + hh) * p.q_sh + cc * 8);
   }
-
-  // ---- first tile: slot ids, then its rows, before q is staged (overlaps the latencies)
+  __builtin_amdgcn_sched_barrier(0);
   u32x4 ldA[NLD];
   uint32_t vmA = 0;
-  int vidx_next = load_idx(0);
-  int vidx_next2 = load_idx(1);
   issue(ldA, vmA, vidx_next);   // unconditional: past the split every row reads as zero
   vidx_next = vidx_next2;
 
