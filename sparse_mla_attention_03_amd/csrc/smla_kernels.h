@@ -23,7 +23,8 @@ struct FwdParams {
   float sm_scale, kv_scale;
   uint16_t* out;                // bf16 [T, H, 512]
   float* lse;                   // fp32 [T, H]
-  float* part_o;                // fp32 [S, T, H, 512] (S > 1)
+  float* part_o;                // fp32 [S, T, H/16, 128, 16, 4] (S > 1): 16-byte column
+                                // chunk c of the 16 heads of a group side by side
   float* part_lse;              // fp32 [S, T, H]      (S > 1)
 };
 

@@ -1,30 +1,32 @@
 // smla_kernels.hip -- gfx950 kernels of libsparsemla.
 //
-// A workgroup (4 wavefronts) owns one unit of work: a query token t, a group
-// of heads and a split s (a contiguous range of t's top-k list).  Two kernels
-// share the building blocks:
+// A workgroup owns one unit of work: a query token t, a group of heads and a
+// split s (a contiguous range of t's top-k list).  Three kernels, by heads per
+// workgroup:
 //
-//   smla_rows_kernel   16-head groups (H = 16, 48, 80, ...).  Each wave streams
-//                      its own 16-row tiles of the split (tiles w, w+4, ...)
-//                      with two tiles in flight in registers and a private LDS
-//                      slot, so the loop has no workgroup barrier; the four
-//                      waves merge their (max, sum, O) once at the end.
-//   smla_tiles_kernel  32- or 64-head groups (H a multiple of 32).  All waves
-//                      share each gathered 64-row tile in LDS, so a row is read
-//                      from HBM once for up to 64 heads.
+//   smla_rows_kernel   16 heads (H not a multiple of 32).  Four waves; each
+//                      streams its own 32-row tiles (16 for bf16 with RoPE) of
+//                      the split through a private LDS slot, one tile in
+//                      flight in registers, no barrier in the loop; the waves
+//                      merge their (max, sum, O) once at the end.
+//   smla_heads_kernel  64 heads (H a multiple of 64).  Eight waves: four score
+//                      waves gather the shared tiles, run QK^T and the softmax
+//                      and write P to LDS; four output waves hold O^T for 128
+//                      columns of all 64 heads and run PV one tile behind.
+//   smla_tiles_kernel  32 heads (H = 32 mod 64).  Four waves share each 64-row
+//                      tile in LDS, one barrier per tile.
 //
-// Per gathered row both run the same steps:
-//   gather   16-byte loads (one 64-lane load covers a 1 KiB bf16 row) into
-//            registers, then into LDS with 16-byte chunks rotated by the row
-//            number (conflict-free column reads).  Invalid entries (padding,
-//            out of range, past the split) read a zero row, never the pool.
+// Per gathered row they run the same steps:
+//   gather   16-byte buffer loads by slot id into registers (out-of-range
+//            ids, padding and entries past the split read zeros, never the
+//            pool), then into LDS with 16-byte chunks permuted by the row
+//            number (conflict-free row and column reads).
 //   QK^T     v_mfma_f32_16x16x32_bf16 (bf16 KV) or v_mfma_f32_16x16x128_f8f6f4
-//            (e4m3 KV, q quantised per tile), rows x heads, fp32 accumulation.
+//            (e4m3 KV, q quantised per 64-head tile), fp32 accumulation.
 //   softmax  online, in registers, log2 domain; a lane owns one head and a
 //            few rows, so the only cross-lane step is a max over 4 lanes.
-//   PV       V = the first 512 columns of the same LDS rows, read 4 or 8 rows x
-//            8 columns per lane and transposed in registers into the MFMA
-//            operand; O^T[dim][head] accumulates in fp32.
+//   PV       V = the first 512 columns of the same LDS rows as the MFMA
+//            operand next to P (bf16); O^T[dim][head] accumulates in fp32.
 //   epilogue S == 1: out = bf16(O * kv_scale / l), lse = ln(sum exp).  S > 1:
 //            normalised fp32 partials + lse per split, merged by the combine
 //            kernel (log-sum-exp weights).
@@ -36,6 +38,13 @@
 #include "smla_kernels.h"
 
 namespace smla {
+
+// Split partials are fp32 chunks of 4 columns; chunk c (columns 4c .. 4c+3) of
+// the 16 heads of a group sit side by side, so the 16 lanes that hold one chunk
+// of 16 consecutive heads store 256 contiguous bytes.  Index in 16-byte units.
+__device__ __forceinline__ int64_t part_chunk(const FwdParams& p, int s, int t, int head, int c) {
+  return (((int64_t)s * p.T + t) * p.H + (head & ~15)) * (kDV / 4) + 16 * c + (head & 15);
+}
 
 // Stand-in for the rows of invalid top-k entries: all zero, never written.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[2048];
@@ -425,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) dst[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
     } else {
-      f32x4* dst = reinterpret_cast<f32x4*>(p.part_o + ((int64_t)s * p.T * p.H + th) * kDV + d0);
+      f32x4* dst = reinterpret_cast<f32x4*>(p.part_o) + part_chunk(p, s, t, head, d0 / 4);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         f32x4 v;
@@ -434,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
           const int j = 4 * k + x;
           v[x] = O[a][j & 7][j >> 3] * scale;
         }
-        dst[k] = v;
+        dst[16 * k] = v;
       }
     }
   }
@@ -881,6 +890,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   }
   if (g == 0) { s_m[wave][m16] = m_run; s_l[wave][m16] = l_w; }
   __syncthreads();
+  // weights of the four waves for head m16
   float M = s_m[0][m16];
 #pragma unroll
   for (int w = 1; w < 4; ++w) M = fmaxf(M, s_m[w][m16]);
@@ -892,38 +902,45 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   }
   const bool any = Lsum > 0.0f;
   const float scale = any ? p.kv_scale / Lsum : 0.0f;
-  const float lse_nat = any ? (M + __builtin_amdgcn_logf(Lsum)) * kLn2 : -INFINITY;
-  const int64_t th = (int64_t)t * p.H + head;
-  const int d0 = 128 * wave + 32 * g;   // this lane's 32 columns of head `head`
-  float acc[32];
-#pragma unroll
-  for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float* src = ob + (w * 16 + m16) * OPAD + d0;
+  if (p.S > 1) {
+    // 32 chunks x 16 heads of this wave's 128 columns, 8 per lane: store k
+    // takes chunk 32 wave + 4k + g of head m16, so a store covers 1 KB of
+    // consecutive partials
+    f32x4* dst = reinterpret_cast<f32x4*>(p.part_o) + part_chunk(p, s, t, head, 32 * wave + g);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * k);
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int x = 0; x < 4; ++x) acc[4 * k + x] += f[w] * v[x];
+      for (int w = 0; w < 4; ++w)
+        v += f[w] * *reinterpret_cast<const f32x4*>(ob + (w * 16 + m16) * OPAD + 128 * wave + 4 * (4 * k + g));
+      dst[64 * k] = v * scale;
+    }
+  } else {
+    // 16 heads x 16 chunks of 8 columns, 4 per lane: store k takes head 4k + g,
+    // columns 128 wave + 8 m16 .. + 8, so 16 lanes write a head's 256 bytes;
+    // the weights of head 4k + g come from lane 4k + g
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int hh = 4 * k + g;
+      float fk[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) fk[w] = __shfl(f[w], hh);
+      const float sk = __shfl(scale, hh);
+      f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float* src = ob + (w * 16 + hh) * OPAD + 128 * wave + 8 * m16;
+        v0 += fk[w] * *reinterpret_cast<const f32x4*>(src);
+        v1 += fk[w] * *reinterpret_cast<const f32x4*>(src + 4);
+      }
+      *reinterpret_cast<u32x4*>(p.out + ((int64_t)t * p.H + h0 + hh) * kDV + 128 * wave + 8 * m16) =
+          u32x4{pack_bf16(v0[0] * sk, v0[1] * sk), pack_bf16(v0[2] * sk, v0[3] * sk),
+                pack_bf16(v1[0] * sk, v1[1] * sk), pack_bf16(v1[2] * sk, v1[3] * sk)};
     }
   }
-  if (p.S == 1) {
-    u32x4* dst = reinterpret_cast<u32x4*>(p.out + th * kDV + d0);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      dst[k] = u32x4{pack_bf16(acc[8 * k] * scale, acc[8 * k + 1] * scale),
-                     pack_bf16(acc[8 * k + 2] * scale, acc[8 * k + 3] * scale),
-                     pack_bf16(acc[8 * k + 4] * scale, acc[8 * k + 5] * scale),
-                     pack_bf16(acc[8 * k + 6] * scale, acc[8 * k + 7] * scale)};
-  } else {
-    f32x4* dst = reinterpret_cast<f32x4*>(p.part_o + ((int64_t)s * p.T * p.H + th) * kDV + d0);
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      dst[k] = f32x4{acc[4 * k] * scale, acc[4 * k + 1] * scale, acc[4 * k + 2] * scale,
-                     acc[4 * k + 3] * scale};
-  }
   if (wave == 0 && g == 0) {
+    const float lse_nat = any ? (M + __builtin_amdgcn_logf(Lsum)) * kLn2 : -INFINITY;
+    const int64_t th = (int64_t)t * p.H + head;
     if (p.S == 1) p.lse[th] = lse_nat;
     else p.part_lse[(int64_t)s * p.T * p.H + th] = lse_nat;
   }
@@ -1446,7 +1463,7 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
           dst[k] = u32x4{w4[0], w4[1], w4[2], w4[3]};
         }
       } else {
-        f32x4* dst = reinterpret_cast<f32x4*>(p.part_o + ((int64_t)s * p.T * p.H + th) * kDV + d0);
+        f32x4* dst = reinterpret_cast<f32x4*>(p.part_o) + part_chunk(p, s, t, h0 + 16 * hb + m16, d0 / 4);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           f32x4 v;
@@ -1455,7 +1472,7 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
             const int jx = 4 * k + x;
             v[x] = O[jx & 7][hb][jx >> 3] * scale;
           }
-          dst[k] = v;
+          dst[16 * k] = v;
         }
       }
     }
@@ -1463,17 +1480,24 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
 }
 
 // ---- split merge: out = sum_s w_s * O_s / sum_s w_s, w_s = exp(lse_s - max) ----
-// One (token, head) pair per 128 threads, 4 columns per thread.  The lse and
-// partial loads of up to 8 splits are issued together (an empty split's
-// partial is loaded but its weight selects zero), so a call costs one memory
-// round trip for S <= 8.
+// One workgroup per (token, 16-head group, 64 columns): thread (chunk tid >> 4,
+// head tid & 15) reads consecutive partials, so each split's 4 KB of the
+// workgroup arrive as whole lines.  The lse and partial loads of up to 8
+// splits are issued together (an empty split's partial is loaded but its
+// weight selects zero), so S <= 8 costs one memory round trip.  The bf16
+// result goes through LDS so that 8 lanes store one head's 128 bytes.
 __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_out[16][64];
+  const int HG = p.H / 16;
+  const int slice = blockIdx.x & 7;
+  const int unit = blockIdx.x >> 3;
+  const int t = unit / HG, grp = unit - t * HG;
+  const int hl = threadIdx.x & 15, cl = threadIdx.x >> 4;
+  const int head = 16 * grp + hl;
   const int64_t TH = (int64_t)p.T * p.H;
-  const int64_t pair = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
-  if (pair >= TH) return;
-  const int d4 = (threadIdx.x & 127) * 4;
-  const float* pl = p.part_lse + pair;
-  const float* po = p.part_o + pair * kDV + d4;
+  const float* pl = p.part_lse + (int64_t)t * p.H + head;
+  const f32x4* po = reinterpret_cast<const f32x4*>(p.part_o) + part_chunk(p, 0, t, head, 16 * slice + cl);
+  const int64_t sstride = TH * (kDV / 4);   // one split's partials, 16-byte units
   constexpr int B = 8;
   float M = -INFINITY, W = 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1484,7 +1508,7 @@ __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
     for (int j = 0; j < B; ++j) {
       const int sj = min(s0 + j, p.S - 1);
       ls[j] = (s0 + j < p.S) ? pl[sj * TH] : -INFINITY;
-      v[j] = *reinterpret_cast<const f32x4*>(po + sj * TH * kDV);
+      v[j] = po[sj * sstride];
     }
     float mb = M;
 #pragma unroll
@@ -1503,15 +1527,17 @@ __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
       acc += live ? w * v[j] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  u32x2* dst = reinterpret_cast<u32x2*>(p.out + pair * kDV + d4);
-  if (M == -INFINITY) {
-    *dst = u32x2{0u, 0u};
-    if (d4 == 0) p.lse[pair] = -INFINITY;
-    return;
+  const float inv = (M == -INFINITY) ? 0.0f : 1.0f / W;   // all splits empty: +0
+  *reinterpret_cast<u32x2*>(&s_out[hl][4 * cl]) =
+      u32x2{pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
+  if (slice == 0 && cl == 0)
+    p.lse[(int64_t)t * p.H + head] = (M == -INFINITY) ? -INFINITY : M + __builtin_amdgcn_logf(W) * kLn2;
+  __syncthreads();
+  if (threadIdx.x < 128) {
+    const int h = threadIdx.x >> 3, k8 = threadIdx.x & 7;
+    *reinterpret_cast<u32x4*>(p.out + ((int64_t)t * p.H + 16 * grp + h) * kDV + 64 * slice + 8 * k8) =
+        *reinterpret_cast<const u32x4*>(&s_out[h][8 * k8]);
   }
-  const float inv = 1.0f / W;
-  *dst = u32x2{pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
-  if (d4 == 0) p.lse[pair] = M + __builtin_amdgcn_logf(W) * kLn2;
 }
 
 // ---- the per-tile q quantisation alone: one workgroup per (token, 64-head tile)
@@ -1578,8 +1604,7 @@ hipError_t launch_fwd(const FwdParams& p, bool kv_fp8, int dqk, hipStream_t stre
 }
 
 hipError_t launch_combine(const FwdParams& p, hipStream_t stream) {
-  const int64_t TH = (int64_t)p.T * p.H;
-  const dim3 gd((unsigned)((TH + 1) / 2)), bd(kThreads);
+  const dim3 gd((unsigned)((int64_t)p.T * (p.H / 16) * 8)), bd(kThreads);
   hipLaunchKernelGGL(smla_combine_kernel, gd, bd, 0, stream, p);
   return hipGetLastError();
 }
