@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 1
+#define SMLA_ABI_VERSION 2
 #define SMLA_DV 512          /* width of V and of out */
 #define SMLA_MAX_SPLITS 64   /* upper bound on the split-K factor */
 
@@ -63,14 +63,33 @@ typedef enum {
   SMLA_KV_FP8_E4M3 = 1       /* kv_pool holds OCP e4m3 ("e4m3fn") codes */
 } smla_kv_dtype_t;
 
+/* Precision of the QK dots for e4m3 KV (options.dot_precision).  For bf16
+ * KV the dots are always bf16 and this must be SMLA_DOTS_DEFAULT. */
+typedef enum {
+  SMLA_DOTS_DEFAULT = 0,     /* e4m3 KV: e4m3 dots with per-tile q quantisation */
+  SMLA_DOTS_BF16 = 1         /* e4m3 KV: bf16 dots, q as given, K dequantised exactly
+                                (the first page, Details: the dot precision is an
+                                optional argument, and bf16 dots carry far less error) */
+} smla_dot_precision_t;
+
 typedef struct {
   int32_t num_splits;        /* split-K factor over each top-k list; 0 = automatic,
                                 otherwise 1..SMLA_MAX_SPLITS */
-  int32_t reserved0;         /* must be zero */
+  int32_t dot_precision;     /* smla_dot_precision_t */
   void* kernel_events[2];    /* optional instrumentation: two caller-created hipEvent_t
                                 that take the start and end timestamps of the main
                                 (gather + attention) kernel's own dispatch (not the split
                                 combine); NULL = not recorded */
+  const float* sinks;        /* optional DEVICE fp32 [H]: per-head attention-sink logit
+                                sigma_h, in the units of s_j (finite, or -inf = no sink
+                                for that head); NULL = no sinks.  The sink joins the
+                                softmax normaliser only, as a key whose value row is zero
+                                (the first page, Details, Limitations: sinks are passed
+                                through to the kernel):
+                                  lse = ln(exp(sigma_h) + sum_j exp(s_j))
+                                  out = sum_j exp(s_j - lse) * kv_scale * row_j[0:512]
+                                so a token with no valid entry gets out = +0 and
+                                lse = sigma_h. */
   int32_t reserved[4];       /* must be zero */
 } smla_options_t;
 

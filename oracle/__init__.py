@@ -66,7 +66,7 @@ def _load():
         c_p, ctypes.c_int, c_i64,
         c_p, c_i64, c_i64,
         ctypes.c_double, ctypes.c_double, ctypes.c_int,
-        c_p, c_p]
+        c_p, c_p, c_p]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -115,12 +115,14 @@ def quantize_q(q: np.ndarray):
 
 
 def sparse_mla_fwd(q: np.ndarray, kv: np.ndarray, idx: np.ndarray,
-                   sm_scale: float, kv_scale: float, q_mode: int = Q_TILE_FP8):
+                   sm_scale: float, kv_scale: float, q_mode: int = Q_TILE_FP8,
+                   sinks: np.ndarray | None = None):
     """Return (out fp64 [T,H,512], lse fp64 [T,H]).
 
     ``q_mode`` matters only for e4m3 KV: Q_TILE_FP8 reproduces the per-tile q
     quantisation of the FP8-dots path, Q_EXACT keeps q exact.
     sm_scale / kv_scale are rounded to fp32 first, as the library receives them.
+    ``sinks``: optional [H] per-head sink logits, rounded to fp32 likewise.
     """
     lib = _load()
     assert q.dtype == np.uint16 and q.ndim == 3
@@ -143,6 +145,10 @@ def sparse_mla_fwd(q: np.ndarray, kv: np.ndarray, idx: np.ndarray,
     if K > 0:
         assert isk == 1
     N = kv2.shape[0]
+    sk = None
+    if sinks is not None:
+        sk = np.ascontiguousarray(np.asarray(sinks, dtype=np.float32).astype(np.float64))
+        assert sk.shape == (H,)
     out = np.empty((T, H, 512), dtype=np.float64)
     lse = np.empty((T, H), dtype=np.float64)
     rc = lib.oracle_sparse_mla_fwd(
@@ -150,7 +156,7 @@ def sparse_mla_fwd(q: np.ndarray, kv: np.ndarray, idx: np.ndarray,
         kv2.ctypes.data, kv_dtype, N,
         idx.ctypes.data if idx.size else None, K, ist,
         float(np.float32(sm_scale)), float(np.float32(kv_scale)), int(q_mode),
-        out.ctypes.data, lse.ctypes.data)
+        sk.ctypes.data if sk is not None else None, out.ctypes.data, lse.ctypes.data)
     if rc != 0:
         raise RuntimeError(f"oracle_sparse_mla_fwd failed with code {rc}")
     return out, lse

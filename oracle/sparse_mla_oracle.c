@@ -105,7 +105,7 @@ int oracle_sparse_mla_fwd(const uint16_t* q, int64_t T, int64_t H, int64_t Dqk,
                           const void* kv, int kv_dtype, int64_t N,
                           const int32_t* idx, int64_t K, int64_t idx_stride_t,
                           double sm_scale, double kv_scale, int q_mode,
-                          double* out, double* lse) {
+                          const double* sinks, double* out, double* lse) {
   const int64_t DV = 512;
   if (T < 0 || H <= 0 || Dqk < DV || K < 0 || N < 0) return 1;
   if (kv_dtype != ORACLE_KV_BF16 && kv_dtype != ORACLE_KV_FP8_E4M3) return 2;
@@ -150,9 +150,11 @@ int oracle_sparse_mla_fwd(const uint16_t* q, int64_t T, int64_t H, int64_t Dqk,
             int64_t r = idx[t * idx_stride_t + k];
             if (r >= 0 && r < N) rows[n++] = r;
           }
+          /* the head's sink logit (-inf = none): a key with a zero value row */
+          const double sig = sinks ? sinks[h] : -INFINITY;
           if (n == 0) {
             for (int64_t d = 0; d < DV; ++d) o[d] = 0.0;
-            lse[t * H + h] = -INFINITY;
+            lse[t * H + h] = sig;
             continue;
           }
           /* 2. the query vector as the dots see it */
@@ -174,10 +176,11 @@ int oracle_sparse_mla_fwd(const uint16_t* q, int64_t T, int64_t H, int64_t Dqk,
             }
             s[j] = sm_scale * acc;
           }
-          /* 4. softmax normaliser, natural log */
+          /* 4. softmax normaliser, natural log, over the entries and the sink */
           double m = s[0];
           for (int64_t j = 1; j < n; ++j) if (s[j] > m) m = s[j];
-          double l = 0.0;
+          if (sig > m) m = sig;
+          double l = exp(sig - m);
           for (int64_t j = 0; j < n; ++j) l += exp(s[j] - m);
           double L = m + log(l);
           lse[t * H + h] = L;

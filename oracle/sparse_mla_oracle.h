@@ -20,6 +20,13 @@
  *     out   = sum_j exp(s_j - lse) * kv_scale * dec(kv[idx_j, 0:512])
  *   J empty -> out = 0, lse = -inf.
  *
+ *   With attention sinks (same first page, Details, Limitations: sinks are
+ *   passed through to the kernel; read here as the usual definition, a
+ *   per-head logit sigma_h that joins the normaliser only, as a key whose
+ *   value row is zero):
+ *     lse   = log(exp(sigma_h) + sum_j exp(s_j)),  out as above with this lse;
+ *     J empty -> out = 0, lse = sigma_h.
+ *
  *   qhat is q itself (exact) for bf16 KV and in mode ORACLE_Q_EXACT; for fp8
  *   KV in mode ORACLE_Q_TILE_FP8 it is q quantised per tile to OCP e4m3 (the
  *   "FP8 dots" path, where the kernel quantises q per tile):
@@ -66,6 +73,8 @@ void oracle_quantize_q_tiles(const uint16_t* q, int64_t T, int64_t H, int64_t Dq
 /* The forward pass, fp64 throughout.
  * kv: [N, Dqk] rows of bf16 bits (kv_dtype 0) or e4m3 codes (kv_dtype 1).
  * idx: int32, entry (t,k) at idx[t*idx_stride_t + k].
+ * sinks: NULL, or fp64 [H] per-head sink logits (-inf = none for that head); a
+ * sink joins the softmax normaliser as a key whose value row is zero.
  * out: fp64 [T, H, 512] contiguous; lse: fp64 [T, H].
  * Returns 0 on success, nonzero on bad arguments. */
 int oracle_sparse_mla_fwd(const uint16_t* q, int64_t T, int64_t H, int64_t Dqk,
@@ -73,7 +82,7 @@ int oracle_sparse_mla_fwd(const uint16_t* q, int64_t T, int64_t H, int64_t Dqk,
                           const void* kv, int kv_dtype, int64_t N,
                           const int32_t* idx, int64_t K, int64_t idx_stride_t,
                           double sm_scale, double kv_scale, int q_mode,
-                          double* out, double* lse);
+                          const double* sinks, double* out, double* lse);
 
 /* Number of OpenMP threads the oracle will use (1 when built without it). */
 int oracle_num_threads(void);

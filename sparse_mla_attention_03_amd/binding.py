@@ -20,6 +20,9 @@ KV_BF16 = 0
 KV_FP8_E4M3 = 1
 DV = 512
 MAX_SPLITS = 64
+DOTS_DEFAULT = 0
+DOTS_BF16 = 1
+ABI_VERSION = 2
 
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_DTYPE",
                 4: "SMLA_ERR_ALIGN", 5: "SMLA_ERR_INVALID_ARG", 6: "SMLA_ERR_UNSUPPORTED",
@@ -34,8 +37,9 @@ class SparseMLAError(RuntimeError):
 
 
 class Options(ctypes.Structure):
-    _fields_ = [("num_splits", ctypes.c_int32), ("reserved0", ctypes.c_int32),
-                ("kernel_events", ctypes.c_void_p * 2), ("reserved", ctypes.c_int32 * 4)]
+    _fields_ = [("num_splits", ctypes.c_int32), ("dot_precision", ctypes.c_int32),
+                ("kernel_events", ctypes.c_void_p * 2), ("sinks", ctypes.c_void_p),
+                ("reserved", ctypes.c_int32 * 4)]
 
 
 _lib = None
@@ -71,6 +75,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sparse_mla_abi_version.argtypes = []
     lib.sparse_mla_abi_version.restype = i32
     if path is None:
+        v = lib.sparse_mla_abi_version()
+        if v != ABI_VERSION:
+            raise SparseMLAError(8, f"{p} has ABI version {v}, this binding needs {ABI_VERSION}; rebuild it")
         _lib = lib
     return lib
 
@@ -130,11 +137,14 @@ def _pool_shape(kv_pool: torch.Tensor):
 def sparse_mla_fwd_ex(q: torch.Tensor, kv_pool: torch.Tensor, topk_idx: torch.Tensor,
                       sm_scale: float, kv_scale: float = 1.0, out: torch.Tensor | None = None,
                       lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                      num_splits: int = 0, stream=None, kernel_events=None):
+                      num_splits: int = 0, stream=None, kernel_events=None,
+                      sinks: torch.Tensor | None = None, dot_precision: int = 0):
     """Sparse MLA forward; returns (out bf16 [T,H,512], lse fp32 [T,H]).
 
     kernel_events: optional pair of raw hipEvent_t handles (ints) the library
-    records around its main kernel (instrumentation for benchmarks)."""
+    records around its main kernel (instrumentation for benchmarks).
+    sinks: optional float32 [H] per-head sink logits on q's device.
+    dot_precision: DOTS_DEFAULT or DOTS_BF16 (e4m3 KV only)."""
     lib = load_library()
     if q.dim() != 3 or q.dtype != torch.bfloat16:
         raise TypeError("q must be bfloat16 [T, H, Dqk]")
@@ -175,6 +185,13 @@ def sparse_mla_fwd_ex(q: torch.Tensor, kv_pool: torch.Tensor, topk_idx: torch.Te
             ws_bytes = workspace.numel() * workspace.element_size()
     opts = Options()
     opts.num_splits = num_splits
+    opts.dot_precision = dot_precision
+    if sinks is not None:
+        if sinks.shape != (H,) or sinks.dtype != torch.float32 or not sinks.is_contiguous():
+            raise ValueError("sinks must be a contiguous float32 [H] tensor")
+        if sinks.device != q.device:
+            raise ValueError(f"sinks is on {sinks.device}, q on {q.device}")
+        opts.sinks = sinks.data_ptr()
     if kernel_events is not None:
         opts.kernel_events[0], opts.kernel_events[1] = kernel_events
     st = lib.sparse_mla_fwd_ex(

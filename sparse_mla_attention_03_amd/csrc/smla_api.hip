@@ -125,7 +125,13 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
   int32_t req = 0;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (opts) {
-    if (opts->reserved0 != 0) return fail(SMLA_ERR_INVALID_ARG, "options.reserved0 must be 0");
+    if (opts->dot_precision != SMLA_DOTS_DEFAULT && opts->dot_precision != SMLA_DOTS_BF16)
+      return fail(SMLA_ERR_INVALID_ARG, "options.dot_precision=%d unknown", opts->dot_precision);
+    if (opts->dot_precision == SMLA_DOTS_BF16 && kv_dtype != SMLA_KV_FP8_E4M3)
+      return fail(SMLA_ERR_INVALID_ARG, "options.dot_precision selects bf16 dots for e4m3 KV only");
+    if (opts->dot_precision == SMLA_DOTS_BF16)
+      return fail(SMLA_ERR_UNSUPPORTED, "bf16 dots on e4m3 KV are not built");
+    if (opts->sinks && !aligned(opts->sinks, 4)) return fail(SMLA_ERR_ALIGN, "sinks must be 4-byte aligned");
     for (int i = 0; i < 4; ++i)
       if (opts->reserved[i] != 0) return fail(SMLA_ERR_INVALID_ARG, "options.reserved[%d] must be 0", i);
     req = opts->num_splits;
@@ -173,6 +179,7 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
   p.kv_scale = kv_scale;
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;
+  p.sinks = opts ? opts->sinks : nullptr;
   if (plan.S > 1) {
     p.part_o = static_cast<float*>(workspace);
     p.part_lse = p.part_o + (size_t)plan.S * T * H * smla::kDV;

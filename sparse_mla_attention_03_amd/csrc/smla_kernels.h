@@ -26,6 +26,7 @@ struct FwdParams {
   float* part_o;                // fp32 [S, T, H/16, 128, 16, 4] (S > 1): 16-byte column
                                 // chunk c of the 16 heads of a group side by side
   float* part_lse;              // fp32 [S, T, H]      (S > 1)
+  const float* sinks;           // fp32 [H] per-head sink logits (natural log), or null
 };
 
 // Heads per workgroup for a head count (a multiple of 16).

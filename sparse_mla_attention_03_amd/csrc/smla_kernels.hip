@@ -46,6 +46,26 @@ __device__ __forceinline__ int64_t part_chunk(const FwdParams& p, int s, int t, 
   return (((int64_t)s * p.T + t) * p.H + (head & ~15)) * (kDV / 4) + 16 * c + (head & 15);
 }
 
+// Sink logit of a head in log2 units; only the final normalisation of an
+// unsplit call takes it (with splits the combine does).  -inf = no sink.
+__device__ __forceinline__ float sink_log2(const FwdParams& p, int head) {
+  return (p.S == 1 && p.sinks != nullptr) ? p.sinks[head] * kLog2e : -INFINITY;
+}
+
+// Final normalisation of one (token, head): m = the running max and l = the
+// sum of exp2(s - m) over the valid entries (log2 units; m = -inf if there is
+// none), s2 = the sink logit (log2 units, -inf = none), which joins the
+// normaliser as a key whose value row is zero.  Returns {multiplier of the
+// accumulated O, including kv_scale; natural-log lse}; {0, -inf} when there
+// is neither a valid entry nor a sink.
+__device__ __forceinline__ float2 finish_row(float m, float l, float s2, float kv_scale) {
+  const float M = fmaxf(m, s2);
+  if (M == -INFINITY) return float2{0.0f, -INFINITY};
+  const float a = __builtin_amdgcn_exp2f(m - M);   // 1 without a sink, 0 without entries
+  const float L = l * a + __builtin_amdgcn_exp2f(s2 - M);
+  return float2{kv_scale * a / L, (M + __builtin_amdgcn_logf(L)) * kLn2};
+}
+
 // Stand-in for the rows of invalid top-k entries: all zero, never written.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[2048];
 
@@ -415,10 +435,9 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
   }
 
   // ---- epilogue ---------------------------------------------------------------
-  const float l = group4_sum(l_run);
-  const bool any = l > 0.0f;
-  const float scale = any ? p.kv_scale / l : 0.0f;
-  const float lse_nat = any ? (m_run + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+  const float2 nz = finish_row(m_run, group4_sum(l_run), sink_log2(p, head), p.kv_scale);
+  const float scale = nz.x;
+  const float lse_nat = nz.y;
   const int64_t th = (int64_t)t * p.H + head;
 #pragma unroll
   for (int a = 0; a < NSLOT; ++a) {
@@ -900,8 +919,8 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
     f[w] = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][m16] - M);
     Lsum += f[w] * s_l[w][m16];
   }
-  const bool any = Lsum > 0.0f;
-  const float scale = any ? p.kv_scale / Lsum : 0.0f;
+  const float2 nz = finish_row(M, Lsum, sink_log2(p, head), p.kv_scale);
+  const float scale = nz.x;
   if (p.S > 1) {
     // 32 chunks x 16 heads of this wave's 128 columns, 8 per lane: store k
     // takes chunk 32 wave + 4k + g of head m16, so a store covers 1 KB of
@@ -939,10 +958,9 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
     }
   }
   if (wave == 0 && g == 0) {
-    const float lse_nat = any ? (M + __builtin_amdgcn_logf(Lsum)) * kLn2 : -INFINITY;
     const int64_t th = (int64_t)t * p.H + head;
-    if (p.S == 1) p.lse[th] = lse_nat;
-    else p.part_lse[(int64_t)s * p.T * p.H + th] = lse_nat;
+    if (p.S == 1) p.lse[th] = nz.y;
+    else p.part_lse[(int64_t)s * p.T * p.H + th] = nz.y;
   }
 }
 
@@ -977,7 +995,7 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
   __shared__ uint32_t s_mask[3][4];        // validity bits of each score wave's rows, per stage
   __shared__ float s_alpha[2][64];         // rescale factor of O per head (when flagged)
   __shared__ int s_flag[2][4];             // score wave w moved its heads' reference max
-  __shared__ float s_lfin[64];             // final softmax denominators
+  __shared__ float s_lfin[64];             // final multipliers of O (kv_scale / denominator)
   __shared__ float s_red[4];
 
   const int tid = threadIdx.x;
@@ -1328,15 +1346,13 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     }
 
     // ---- the output waves need the denominators; this wave writes lse
-    const float l = group4_sum(l_run);
-    if (g == 0) s_lfin[16 * qw + m16] = l;
+    const float2 nz = finish_row(m_run, group4_sum(l_run), sink_log2(p, head), p.kv_scale);
+    if (g == 0) s_lfin[16 * qw + m16] = nz.x;
     __syncthreads();   // pairs with the output waves' last PV phase
     if (g == 0) {
-      const bool any = l > 0.0f;
-      const float lse_nat = any ? (m_run + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
       const int64_t th = (int64_t)t * p.H + head;
-      if (p.S == 1) p.lse[th] = lse_nat;
-      else p.part_lse[(int64_t)s * p.T * p.H + th] = lse_nat;
+      if (p.S == 1) p.lse[th] = nz.y;
+      else p.part_lse[(int64_t)s * p.T * p.H + th] = nz.y;
     }
   } else {
     // =============================== output waves ==============================
@@ -1447,8 +1463,7 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     const int d0 = 128 * pw + 32 * g;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
-      const float Lsum = s_lfin[16 * hb + m16];
-      const float scale = Lsum > 0.0f ? p.kv_scale / Lsum : 0.0f;
+      const float scale = s_lfin[16 * hb + m16];
       const int64_t th = (int64_t)t * p.H + h0 + 16 * hb + m16;
       if (p.S == 1) {
         u32x4* dst = reinterpret_cast<u32x4*>(p.out + th * kDV + d0);
@@ -1499,7 +1514,9 @@ __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
   const f32x4* po = reinterpret_cast<const f32x4*>(p.part_o) + part_chunk(p, 0, t, head, 16 * slice + cl);
   const int64_t sstride = TH * (kDV / 4);   // one split's partials, 16-byte units
   constexpr int B = 8;
-  float M = -INFINITY, W = 0.0f;
+  // a sink enters as one more split whose partial is zero: weight exp(sink - M)
+  float M = p.sinks ? p.sinks[head] : -INFINITY;
+  float W = (M == -INFINITY) ? 0.0f : 1.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < p.S; s0 += B) {
     float ls[B];

@@ -57,7 +57,7 @@ TOL_LSE = 1e-3                             # max |lse - oracle| on rows with a v
 TOL_REL_L2 = {"bf16": 5e-3, "fp8": 1e-2}   # secondary: relative L2 of out
 
 
-def oracle_for_tokens(case, tokens=None, q_mode=None, idx=None):
+def oracle_for_tokens(case, tokens=None, q_mode=None, idx=None, sinks=None):
     """Oracle result for a subset of tokens, gathering only the rows they use.
 
     The rows named by the selected tokens' lists are copied to the host, the
@@ -84,7 +84,7 @@ def oracle_for_tokens(case, tokens=None, q_mode=None, idx=None):
         q_mode = oracle.Q_TILE_FP8
     return oracle.sparse_mla_fwd(np.ascontiguousarray(q), np.ascontiguousarray(kv),
                                  np.ascontiguousarray(remap), case.sm_scale, case.kv_scale,
-                                 q_mode=q_mode)
+                                 q_mode=q_mode, sinks=sinks)
 
 
 def compare(out, lse, ref_out, ref_lse, kv_dtype, what=""):

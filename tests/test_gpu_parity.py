@@ -318,3 +318,73 @@ def test_full_size_sampled_parity(name):
             ref_out, ref_lse, spec.kv_dtype, name)
     del case
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- attention sinks
+
+def _gpu_sinks(H, seed):
+    """Per-head sinks: normal logits, two heads without a sink, one dominant sink."""
+    s = np.random.default_rng(seed).normal(0.0, 3.0, H).astype(np.float32)
+    s[0] = -np.inf
+    s[H - 1] = -np.inf
+    s[H // 2] = 40.0
+    return s
+
+
+SINK_CASES = [
+    # T, H, Dqk, K, ctx, kv, pad_frac
+    (3, 16, 512, 300, 4096, "bf16", 0.2),     # 16-head kernel
+    (2, 32, 512, 200, 2048, "fp8", 0.0),      # 32-head kernel
+    (2, 64, 576, 190, 1024, "bf16", 0.1),     # 64-head kernel
+    (2, 128, 512, 321, 4096, "fp8", 0.1),
+    (2, 16, 576, 257, 2048, "fp8", 0.5),
+]
+
+
+@pytest.mark.parametrize("T,H,D,K,ctx,kv,pad", SINK_CASES)
+@pytest.mark.parametrize("splits", [1, 0, 3])
+def test_sinks_parity(T, H, D, K, ctx, kv, pad, splits):
+    case = gpu_case(T=T, H=H, Dqk=D, K=K, ctx=ctx, kv_dtype=kv, block_size=64, seed=5 * T + H)
+    idx = case.topk_idx
+    if pad > 0:
+        rng = np.random.default_rng(K + 1)
+        idx = synth.with_padding(idx.cpu().numpy(), rng, pad)
+        idx[0, :] = -1                       # one token with no valid entry
+        idx = torch.from_numpy(idx).to(DEV)
+    sinks = _gpu_sinks(H, T + K)
+    out, lse = sparse_mla_fwd_ex(case.q, case.kv_pool, idx, case.sm_scale, case.kv_scale,
+                                 num_splits=splits, sinks=torch.from_numpy(sinks).to(DEV))
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_for_tokens(case, idx=idx, sinks=sinks)
+    compare(out, lse, ref_out, ref_lse, kv, f"sinks T{T} H{H} D{D} {kv} S{splits}")
+
+
+@pytest.mark.parametrize("H", [16, 32, 64])
+@pytest.mark.parametrize("splits", [1, 2])
+def test_sinks_without_entries_give_zero_and_the_sink(H, splits):
+    case = gpu_case(T=2, H=H, Dqk=512, K=128, ctx=1024, seed=H)
+    idx = torch.full((2, 128), -1, dtype=torch.int32, device=DEV)
+    sinks = _gpu_sinks(H, 7)
+    out, lse = sparse_mla_fwd_ex(case.q, case.kv_pool, idx, case.sm_scale, 1.0,
+                                 num_splits=splits, sinks=torch.from_numpy(sinks).to(DEV))
+    torch.cuda.synchronize()
+    o = out.view(torch.int16)
+    assert torch.equal(o, torch.zeros_like(o))
+    l = lse.cpu().numpy()
+    want = np.broadcast_to(sinks, (2, H))
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isneginf(l), ~fin)
+    assert np.max(np.abs(l[fin] - want[fin])) <= 1e-6 * 40
+
+
+@pytest.mark.parametrize("H,kv", [(16, "bf16"), (32, "fp8"), (128, "bf16")])
+@pytest.mark.parametrize("splits", [1, 0])
+def test_sinks_of_minus_infinity_are_bitwise_no_sinks(H, kv, splits):
+    case = gpu_case(T=3, H=H, Dqk=512, K=200, ctx=2048, kv_dtype=kv, seed=11)
+    a = run(case, num_splits=splits)
+    b = sparse_mla_fwd_ex(case.q, case.kv_pool, case.topk_idx, case.sm_scale, case.kv_scale,
+                          num_splits=splits,
+                          sinks=torch.full((H,), -math.inf, dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])

@@ -333,3 +333,67 @@ def test_fp8_q_quantisation_effect_in_pages_band():
     out_a, _ = _fwd(case, mode=oracle.Q_EXACT)
     err = rel_l2(out_b, out_a)
     assert 0.5 * lo < err < 1.5 * hi, err
+
+
+# ---------------------------------------------------------------- attention sinks
+
+def _sinks(H, seed, neg_inf_heads=()):
+    s = np.random.default_rng(seed).normal(0.0, 2.0, H).astype(np.float32)
+    s[list(neg_inf_heads)] = -np.inf
+    return s
+
+
+@pytest.mark.parametrize("D,H", [(512, 16), (576, 64)])
+def test_sinks_equal_a_zero_value_logit_column(D, H):
+    # dense attention by library routines with one more logit column per head
+    # (the sink) whose value row is zero
+    case = _case(T=3, H=H, D=D, ctx=256, seed=21)
+    N = case.spec.N
+    idx = np.stack([np.random.default_rng(t).permutation(N) for t in range(3)]).astype(np.int32)
+    sinks = _sinks(H, 22, neg_inf_heads=(1, 5))
+    out, lse = oracle.sparse_mla_fwd(bits16(case.q), kv_bits(case.kv_pool), idx, case.sm_scale,
+                                     case.kv_scale, sinks=sinks)
+    q = case.q.to(torch.float64)                                        # [T, H, D]
+    kvv = torch.from_numpy(kv_values_f64(case.kv_pool, 1.0))            # [N, D]
+    logits = torch.matmul(q, kvv.T.contiguous()) * float(np.float32(case.sm_scale))
+    sig = torch.from_numpy(sinks.astype(np.float64)).view(1, H, 1).expand(3, H, 1)
+    full = torch.cat([logits, sig], dim=-1)                             # [T, H, N + 1]
+    p = torch.softmax(full, dim=-1)[..., :N]
+    ref_out = torch.matmul(p, kvv[:, :512].contiguous()).numpy()
+    ref_lse = torch.logsumexp(full, dim=-1).numpy()
+    assert np.max(np.abs(out - ref_out)) < 1e-12
+    assert np.max(np.abs(lse - ref_lse)) < 1e-12
+
+
+def test_sinks_single_index_closed_form():
+    case = _case(T=1, H=16, K=6, seed=23)
+    kvv = kv_values_f64(case.kv_pool, 1.0)
+    r = 91
+    idx = np.array([[-1, r, -1, -1, -1, -1]], np.int32)
+    sinks = _sinks(16, 24)
+    out, lse = oracle.sparse_mla_fwd(bits16(case.q), kv_bits(case.kv_pool), idx, case.sm_scale,
+                                     1.0, sinks=sinks)
+    s = case.q[0].to(torch.float64).numpy() @ kvv[r] * float(np.float32(case.sm_scale))
+    sig = sinks.astype(np.float64)
+    w = 1.0 / (1.0 + np.exp(sig - s))                  # the entry's share against the sink
+    assert np.max(np.abs(out[0] - w[:, None] * kvv[r, :512])) < 1e-12
+    assert np.max(np.abs(lse[0] - np.logaddexp(s, sig))) < 1e-12
+
+
+def test_sinks_all_padding_gives_zero_and_the_sink():
+    case = _case(T=2, K=8, seed=25)
+    sinks = _sinks(16, 26, neg_inf_heads=(0, 9))
+    out, lse = oracle.sparse_mla_fwd(bits16(case.q), kv_bits(case.kv_pool),
+                                     np.full((2, 8), -1, np.int32), case.sm_scale, 1.0,
+                                     sinks=sinks)
+    assert np.all(out == 0) and not np.any(np.signbit(out))
+    assert np.array_equal(lse, np.broadcast_to(sinks.astype(np.float64), (2, 16)))
+
+
+def test_sinks_of_minus_infinity_change_nothing():
+    case = _case(T=3, K=64, seed=27)
+    idx = synth.with_padding(case.topk_idx.numpy(), np.random.default_rng(3), 0.2)
+    out0, lse0 = _fwd(case, idx=idx)
+    out1, lse1 = oracle.sparse_mla_fwd(bits16(case.q), kv_bits(case.kv_pool), idx, case.sm_scale,
+                                       case.kv_scale, sinks=np.full(16, -np.inf, np.float32))
+    assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
