@@ -123,18 +123,18 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
   if (!std::isfinite(sm_scale) || !std::isfinite(kv_scale))
     return fail(SMLA_ERR_INVALID_ARG, "sm_scale and kv_scale must be finite");
   int32_t req = 0;
+  bool bf16_dots = false;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (opts) {
     if (opts->dot_precision != SMLA_DOTS_DEFAULT && opts->dot_precision != SMLA_DOTS_BF16)
       return fail(SMLA_ERR_INVALID_ARG, "options.dot_precision=%d unknown", opts->dot_precision);
     if (opts->dot_precision == SMLA_DOTS_BF16 && kv_dtype != SMLA_KV_FP8_E4M3)
       return fail(SMLA_ERR_INVALID_ARG, "options.dot_precision selects bf16 dots for e4m3 KV only");
-    if (opts->dot_precision == SMLA_DOTS_BF16)
-      return fail(SMLA_ERR_UNSUPPORTED, "bf16 dots on e4m3 KV are not built");
     if (opts->sinks && !aligned(opts->sinks, 4)) return fail(SMLA_ERR_ALIGN, "sinks must be 4-byte aligned");
     for (int i = 0; i < 4; ++i)
       if (opts->reserved[i] != 0) return fail(SMLA_ERR_INVALID_ARG, "options.reserved[%d] must be 0", i);
     req = opts->num_splits;
+    bf16_dots = opts->dot_precision == SMLA_DOTS_BF16;
     ev0 = static_cast<hipEvent_t>(opts->kernel_events[0]);
     ev1 = static_cast<hipEvent_t>(opts->kernel_events[1]);
     if ((ev0 == nullptr) != (ev1 == nullptr))
@@ -190,7 +190,7 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
             plan.S, plan.rps);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  e = smla::launch_fwd(p, kv_dtype == SMLA_KV_FP8_E4M3, (int)Dqk, s, ev0, ev1);
+  e = smla::launch_fwd(p, kv_dtype == SMLA_KV_FP8_E4M3, bf16_dots, (int)Dqk, s, ev0, ev1);
   if (e != hipSuccess) return fail(SMLA_ERR_HIP, "forward kernel launch: %s", hipGetErrorString(e));
   if (plan.S > 1) {
     e = smla::launch_combine(p, s);

@@ -32,9 +32,10 @@ struct FwdParams {
 // Heads per workgroup for a head count (a multiple of 16).
 inline int heads_per_workgroup(int64_t H) { return (H % 64 == 0) ? 64 : (H % 32 == 0) ? 32 : 16; }
 
-// ev0 / ev1 (both or neither): events that take the main kernel's own start
-// and end timestamps.
-hipError_t launch_fwd(const FwdParams& p, bool kv_fp8, int dqk, hipStream_t stream,
+// bf16_dots: e4m3 KV with bf16 QK dots (kv_fp8 must be set).  ev0 / ev1
+// (both or neither): events that take the main kernel's own start and end
+// timestamps.
+hipError_t launch_fwd(const FwdParams& p, bool kv_fp8, bool bf16_dots, int dqk, hipStream_t stream,
                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_combine(const FwdParams& p, hipStream_t stream);
 hipError_t launch_quantize_q(const uint16_t* q, int64_t q_st, int64_t q_sh, int32_t T, int32_t H,

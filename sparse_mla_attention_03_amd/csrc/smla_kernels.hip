@@ -126,9 +126,13 @@ __device__ __forceinline__ uint32_t tile_rows(int vidx, const uint8_t* kv, int64
   return vm;
 }
 
-template <bool KV8, int DQK, int HT>
+template <bool KV8, int DQK, int HT, bool QB = false>
 __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
   using G = Geom<KV8, DQK>;
+  // QB: e4m3 KV with bf16 QK dots (q as given, K dequantised exactly);
+  // F8: e4m3 dots on the per-tile quantised q
+  constexpr bool F8 = KV8 && !QB;
+  constexpr int NKQ = F8 ? G::NKB : DQK / 32;   // QK k-steps
   constexpr int WH = HT / 16;          // 16-head tiles per workgroup
   constexpr int WD = 4 / WH;           // waves per head tile
   constexpr int DPW = kDV / WD;        // output columns per wave
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
   constexpr int BPW = NBLK / WD;       // QK row blocks per wave
   constexpr int NSTAGE = 2;
   constexpr int SX = (WD > 1) ? WH * NBLK * 16 * 16 * 4 : 0;   // score exchange bytes
-  constexpr int QLDS = KV8 ? HT * DQK : 0;                     // quantised q (prologue only)
+  constexpr int QLDS = F8 ? HT * DQK : 0;                      // quantised q (prologue only)
   constexpr int RING = NSTAGE * G::STAGE;
   static_assert(QLDS <= RING, "q staging must fit in the ring");
 
@@ -176,12 +180,12 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
   // ---- q operand (B of QK^T): lane (m16 = head, g) holds 8 (bf16) or 32 (fp8)
   // columns per k-step; column d of the row maps to the same (k-step, g, slot)
   // in the K fragments below.
-  u32x4 qf[KV8 ? 1 : G::NKB];
-  i32x8 q8[KV8 ? G::NKB : 1];
+  u32x4 qf[F8 ? 1 : NKQ];
+  i32x8 q8[F8 ? G::NKB : 1];
   float c2;   // logit multiplier, log2 domain
-  if constexpr (!KV8) {
+  if constexpr (!F8) {
 #pragma unroll
-    for (int kb = 0; kb < G::NKB; ++kb)
+    for (int kb = 0; kb < NKQ; ++kb)
       qf[kb] = *reinterpret_cast<const u32x4*>(qrow + kb * 32 + 8 * g);
     c2 = p.sm_scale * p.kv_scale * kLog2e;
   } else {
@@ -313,6 +317,17 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
           const u32x4 a = (kb < G::MCH / 4) ? lds_read16(st + lds_main<G>(r, c))
                                             : lds_read16(st + lds_tail<G>(r, c - G::MCH));
           acc = mfma_bf16(a, qf[kb], acc);
+        }
+      } else if constexpr (QB) {
+#pragma unroll
+        for (int kb = 0; kb < NKQ; ++kb) {
+          // e4m3 columns 32kb + 8g .. +8: half of 16-byte chunk 2kb + g/2, widened exactly
+          const int c = 2 * kb + (g >> 1);
+          const int o = (c < G::MCH) ? lds_main<G>(r, c) : lds_tail<G>(r, c - G::MCH);
+          const u32x2 raw = lds_read8(st + o + 8 * (g & 1));
+          const u32x2 lo = e4m3x4_to_bf16x4(raw[0]);
+          const u32x2 hi = e4m3x4_to_bf16x4(raw[1]);
+          acc = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, qf[kb], acc);
         }
       } else {
 #pragma unroll
@@ -484,9 +499,13 @@ constexpr float kSlack = 8.0f;   // log2 headroom of the lazily rescaled running
 // different halves of the bank space.
 __device__ __forceinline__ int row_key(int r) { return ((r & 1) << 3) | ((r >> 1) & 7); }
 
-template <bool KV8, int DQK, int TR>
+template <bool KV8, int DQK, int TR, bool QB = false>
 __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   using G = Geom<KV8, DQK>;
+  // QB: e4m3 KV with bf16 QK dots (q as given, K dequantised exactly);
+  // F8: e4m3 dots on the per-tile quantised q
+  constexpr bool F8 = KV8 && !QB;
+  constexpr int NKQ = F8 ? G::NKB : DQK / 32;             // QK k-steps
   static_assert(TR == 16 || TR == 32, "a wave tile is one or two 16-row blocks");
   constexpr int NB = TR / 16;                             // 16-row blocks per tile
   constexpr int WMAIN = TR * G::MAIN;
@@ -499,7 +518,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   constexpr int TROWS = (G::TCH == 8) ? 8 : 16;           // RoPE part: rows per load
   constexpr int NLDT = G::TCH ? TR / TROWS : 0;           // RoPE loads per tile
   constexpr int NLD = NLDM + NLDT;
-  constexpr int QROW = DQK * (KV8 ? 1 : 2) + 16;          // padded q row (no bank conflicts)
+  constexpr int QROW = DQK * (F8 ? 1 : 2) + 16;           // padded q row (no bank conflicts)
   constexpr int QBYTES = 16 * QROW;                       // the group's q (B operand of QK^T)
   constexpr int OPAD = kDV + 4;                           // padded fp32 row of the merge buffer
   constexpr int MERGE = 4 * 16 * OPAD * 4;                // the four waves' O (after the loop)
@@ -623,7 +642,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   // or e4m3 codes of the per-tile quantised q
   uint8_t* qs = smem + 4 * WSLOT;
   float c2;
-  if constexpr (!KV8) {
+  if constexpr (!F8) {
 #pragma unroll
     for (int r = 0; r < NQ; ++r) {
       const int c = tid + r * kThreads, hh = c / CPR, cc = c - hh * CPR;
@@ -694,9 +713,19 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   // blocks inner, so each q fragment feeds NB MFMAs; two partial sums per
   // block (even / odd k-steps) keep back-to-back MFMAs independent, and the
   // fragments of the next DEPTH k-steps are read ahead of their MFMAs.
-  using KFrag = std::conditional_t<KV8, i32x8, u32x4>;
+  using KFrag = std::conditional_t<F8, i32x8, u32x4>;
   auto kfrag = [&](int b, int kb) -> KFrag {
-    if constexpr (!KV8) {
+    if constexpr (QB) {
+      // e4m3 columns 32kb + 8g .. +8 (8 bytes of a 16-byte chunk), widened to
+      // bf16 exactly; RoPE columns come from the tail part
+      const int r = 16 * b + m16;
+      const int c = 2 * kb + (g >> 1);
+      const int o = (c < G::MCH) ? off_main(r, c) : off_tail(r, c - G::MCH);
+      const u32x2 raw = lds_read8(slot + o + 8 * (g & 1));
+      const u32x2 lo = e4m3x4_to_bf16x4(raw[0]);
+      const u32x2 hi = e4m3x4_to_bf16x4(raw[1]);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    } else if constexpr (!KV8) {
       return (kb < G::MCH / 4) ? lds_read16(slot + 16 * b * G::MAIN + qk_base[kb & 3] + 256 * (kb >> 2))
                                : lds_read16(slot + off_tail(16 * b + m16, 4 * kb + g - G::MCH));
     } else {
@@ -714,7 +743,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
     }
   };
   auto qfrag = [&](int kb) -> KFrag {
-    if constexpr (!KV8) {
+    if constexpr (!F8) {
       return lds_read16(qlane + (kb * 32 + 8 * g) * 2);
     } else {
       const int c = 8 * kb + 2 * g;
@@ -729,7 +758,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   };
   constexpr int DEPTH = 2;
   auto qk = [&](f32x4 (&acc)[NB]) {
-    if constexpr (KV8) {
+    if constexpr (F8) {
       // e4m3: few, wide k-steps (128 columns); the NB blocks are the
       // independent chains
 #pragma unroll
@@ -753,31 +782,31 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
       for (int b = 0; b < NB; ++b) ra[d][b] = kfrag(b, d);
     }
 #pragma unroll
-    for (int kb = 0; kb < G::NKB; ++kb) {
+    for (int kb = 0; kb < NKQ; ++kb) {
       const KFrag bq = rq[kb % DEPTH];
       KFrag a[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) a[b] = ra[kb % DEPTH][b];
-      if (kb + DEPTH < G::NKB) {
+      if (kb + DEPTH < NKQ) {
         rq[kb % DEPTH] = qfrag(kb + DEPTH);
 #pragma unroll
         for (int b = 0; b < NB; ++b) ra[kb % DEPTH][b] = kfrag(b, kb + DEPTH);
       }
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        if constexpr (!KV8) ac[b][kb & 1] = mfma_bf16(a[b], bq, ac[b][kb & 1]);
+        if constexpr (!F8) ac[b][kb & 1] = mfma_bf16(a[b], bq, ac[b][kb & 1]);
         else ac[b][kb & 1] = mfma_fp8(a[b], bq, ac[b][kb & 1]);
       }
     }
-    if constexpr (!KV8) {
+    if constexpr (!F8) {
       // issue order: DEPTH k-steps of reads, then per k-step NB MFMAs and the
       // NB + 1 reads of k-step kb + DEPTH
       constexpr int RPK = NB + 1;
       __builtin_amdgcn_sched_group_barrier(0x100, DEPTH * RPK, 0);
 #pragma unroll
-      for (int kb = 0; kb < G::NKB; ++kb) {
+      for (int kb = 0; kb < NKQ; ++kb) {
         __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
-        if (kb + DEPTH < G::NKB) __builtin_amdgcn_sched_group_barrier(0x100, RPK, 0);
+        if (kb + DEPTH < NKQ) __builtin_amdgcn_sched_group_barrier(0x100, RPK, 0);
       }
     }
 #pragma unroll
@@ -1585,9 +1614,11 @@ __global__ __launch_bounds__(kThreads) void smla_quantize_q_kernel(const uint16_
 }
 
 // ---- launch wrappers ----------------------------------------------------------------
-template <bool KV8, int DQK>
+template <bool KV8, int DQK, bool QB>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  const int HT = heads_per_workgroup(p.H);
+  // bf16 dots on e4m3 KV run in the 16- and 32-head kernels (64-head groups as
+  // two 32-head groups)
+  const int HT = QB ? (p.H % 32 == 0 ? 32 : 16) : heads_per_workgroup(p.H);
   const int HG = p.H / HT;
   const int64_t units = (int64_t)p.T * p.S;
   const int64_t grid = ((units + 7) / 8) * 8 * HG;
@@ -1599,25 +1630,31 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream, hipEvent_
     case 16:
       // 32-row wave tiles where four of them plus q fit in LDS, else 16
       if constexpr (KV8 || DQK == 512)
-        hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 32>), gd, bd, 0, stream, ev0, ev1, 0, p);
+        hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 32, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
       else
-        hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 16>), gd, bd, 0, stream, ev0, ev1, 0, p);
+        hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 16, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
       break;
     case 32:
-      hipExtLaunchKernelGGL((smla_tiles_kernel<KV8, DQK, 32>), gd, bd, 0, stream, ev0, ev1, 0, p);
+      hipExtLaunchKernelGGL((smla_tiles_kernel<KV8, DQK, 32, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
       break;
     default:
-      hipExtLaunchKernelGGL((smla_heads_kernel<KV8, DQK>), gd, dim3(2 * kThreads), 0, stream, ev0, ev1, 0, p);
+      if constexpr (!QB)
+        hipExtLaunchKernelGGL((smla_heads_kernel<KV8, DQK>), gd, dim3(2 * kThreads), 0, stream, ev0, ev1, 0, p);
       break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdParams& p, bool kv_fp8, int dqk, hipStream_t stream, hipEvent_t ev0,
-                      hipEvent_t ev1) {
+hipError_t launch_fwd(const FwdParams& p, bool kv_fp8, bool bf16_dots, int dqk, hipStream_t stream,
+                      hipEvent_t ev0, hipEvent_t ev1) {
+  if (kv_fp8 && bf16_dots)
+    return dqk == 576 ? launch_fwd_t<true, 576, true>(p, stream, ev0, ev1)
+                      : launch_fwd_t<true, 512, true>(p, stream, ev0, ev1);
   if (kv_fp8)
-    return dqk == 576 ? launch_fwd_t<true, 576>(p, stream, ev0, ev1) : launch_fwd_t<true, 512>(p, stream, ev0, ev1);
-  return dqk == 576 ? launch_fwd_t<false, 576>(p, stream, ev0, ev1) : launch_fwd_t<false, 512>(p, stream, ev0, ev1);
+    return dqk == 576 ? launch_fwd_t<true, 576, false>(p, stream, ev0, ev1)
+                      : launch_fwd_t<true, 512, false>(p, stream, ev0, ev1);
+  return dqk == 576 ? launch_fwd_t<false, 576, false>(p, stream, ev0, ev1)
+                    : launch_fwd_t<false, 512, false>(p, stream, ev0, ev1);
 }
 
 hipError_t launch_combine(const FwdParams& p, hipStream_t stream) {

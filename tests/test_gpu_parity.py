@@ -18,7 +18,8 @@ import torch
 import oracle
 from sparse_mla_attention_03_amd import binding, synth
 from sparse_mla_attention_03_amd.binding import sparse_mla_fwd, sparse_mla_fwd_ex
-from tests.helpers import bits16, codes8, compare, kv_values_f64, oracle_for_tokens
+from tests.helpers import (bits16, codes8, compare, kv_values_f64, oracle_for_tokens,
+                           read_golden, rel_l2)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -388,3 +389,48 @@ def test_sinks_of_minus_infinity_are_bitwise_no_sinks(H, kv, splits):
     torch.cuda.synchronize()
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
     assert torch.equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------- bf16 dots on e4m3 KV
+
+BF16_DOT_CASES = [
+    # T, H, Dqk, K, ctx, pad_frac
+    (3, 16, 512, 300, 4096, 0.2),     # 16-head kernel
+    (2, 16, 576, 257, 2048, 0.1),
+    (2, 32, 512, 200, 2048, 0.0),     # 32-head kernel
+    (2, 64, 576, 190, 1024, 0.1),     # 64 heads as two 32-head groups
+    (2, 128, 512, 321, 4096, 0.1),
+]
+
+
+@pytest.mark.parametrize("T,H,D,K,ctx,pad", BF16_DOT_CASES)
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_bf16_dots_parity(T, H, D, K, ctx, pad, splits):
+    """e4m3 KV with bf16 dots against the oracle with q exact, at the bf16 bar."""
+    case = gpu_case(T=T, H=H, Dqk=D, K=K, ctx=ctx, kv_dtype="fp8", block_size=64, seed=3 * T + H + D)
+    idx = case.topk_idx
+    if pad > 0:
+        rng = np.random.default_rng(K + 2)
+        idx = torch.from_numpy(synth.with_padding(idx.cpu().numpy(), rng, pad)).to(DEV)
+    out, lse = sparse_mla_fwd_ex(case.q, case.kv_pool, idx, case.sm_scale, case.kv_scale,
+                                 num_splits=splits, dot_precision=binding.DOTS_BF16)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_for_tokens(case, idx=idx, q_mode=oracle.Q_EXACT)
+    compare(out, lse, ref_out, ref_lse, "bf16", f"bf16 dots T{T} H{H} D{D} S{splits}")
+
+
+def test_dot_precision_errors_match_the_pages():
+    """Relative L2 against exact-q attention: e4m3 dots inside the band the pages
+    print for FP8 dots, bf16 dots no worse than the pages' bf16-dots figure."""
+    band = {r[0]: tuple(map(float, r[1:])) for r in read_golden("pages_numerics.txt")}
+    case = gpu_case(T=4, H=16, Dqk=512, K=2048, ctx=8192, kv_dtype="fp8", seed=16)
+    exact, _ = oracle_for_tokens(case, q_mode=oracle.Q_EXACT)
+    f8, _ = run(case)
+    b16, _ = sparse_mla_fwd_ex(case.q, case.kv_pool, case.topk_idx, case.sm_scale, case.kv_scale,
+                               dot_precision=binding.DOTS_BF16)
+    torch.cuda.synchronize()
+    lo, hi = band["fp8_dots_rel_l2"]
+    e8 = rel_l2(f8.float().cpu().numpy().astype(np.float64), exact)
+    eb = rel_l2(b16.float().cpu().numpy().astype(np.float64), exact)
+    assert 0.5 * lo < e8 < 1.5 * hi, e8
+    assert eb < 1.5 * band["bf16_dots_rel_l2"][1], eb
