@@ -20,7 +20,8 @@
  *   are never read and contribute nothing; duplicates count once per
  *   occurrence.  A token with no valid entry gets out = +0 and lse = -inf.
  *
- *   qhat = q for bf16 KV.  For OCP fp8-e4m3 KV the QK dots run in fp8: q is
+ *   qhat = q for bf16 KV.  For OCP fp8-e4m3 KV the QK dots run in fp8 (unless
+ *   options select bf16 dots or pass q pre-quantised, see smla_options_t): q is
  *   quantised inside the kernel per tile (the first page, Details: "the
  *   kernel quantizes q per tile"), a tile being heads [64g, min(64g+64, H))
  *   of one token over all Dqk columns:  s_q = amax|q| / 448 (fp32; 1 if the
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 2
+#define SMLA_ABI_VERSION 3
 #define SMLA_DV 512          /* width of V and of out */
 #define SMLA_MAX_SPLITS 64   /* upper bound on the split-K factor */
 
@@ -90,7 +91,14 @@ typedef struct {
                                   out = sum_j exp(s_j - lse) * kv_scale * row_j[0:512]
                                 so a token with no valid entry gets out = +0 and
                                 lse = sigma_h. */
-  int32_t reserved[4];       /* must be zero */
+  float q_scale;             /* 0 = q is bf16 (default).  > 0 (finite): q is already
+                                quantised -- it holds OCP e4m3 codes [T, H, Dqk], one byte
+                                per element (strides in bytes, multiples of 16), with
+                                qhat = q_scale * code for every element (one per-tensor
+                                scale; the first page, Details: gfx950 keeps the
+                                pre-quantised q).  e4m3 KV with SMLA_DOTS_DEFAULT only; the
+                                per-tile quantisation is skipped. */
+  int32_t reserved[3];       /* must be zero */
 } smla_options_t;
 
 /*

@@ -28,6 +28,7 @@ KV_BF16 = 0
 KV_FP8_E4M3 = 1
 Q_EXACT = 0
 Q_TILE_FP8 = 1
+Q_GIVEN_FP8 = 2
 
 _lib = None
 
@@ -65,7 +66,7 @@ def _load():
         c_p, c_i64, c_i64, c_i64, c_i64, c_i64,
         c_p, ctypes.c_int, c_i64,
         c_p, c_i64, c_i64,
-        ctypes.c_double, ctypes.c_double, ctypes.c_int,
+        ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_double,
         c_p, c_p, c_p]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
@@ -116,16 +117,17 @@ def quantize_q(q: np.ndarray):
 
 def sparse_mla_fwd(q: np.ndarray, kv: np.ndarray, idx: np.ndarray,
                    sm_scale: float, kv_scale: float, q_mode: int = Q_TILE_FP8,
-                   sinks: np.ndarray | None = None):
+                   sinks: np.ndarray | None = None, q_scale: float = 0.0):
     """Return (out fp64 [T,H,512], lse fp64 [T,H]).
 
     ``q_mode`` matters only for e4m3 KV: Q_TILE_FP8 reproduces the per-tile q
     quantisation of the FP8-dots path, Q_EXACT keeps q exact.
     sm_scale / kv_scale are rounded to fp32 first, as the library receives them.
     ``sinks``: optional [H] per-head sink logits, rounded to fp32 likewise.
+    ``q_mode = Q_GIVEN_FP8``: q holds e4m3 codes (uint8), qhat = q_scale * code.
     """
     lib = _load()
-    assert q.dtype == np.uint16 and q.ndim == 3
+    assert q.dtype == (np.uint8 if q_mode == Q_GIVEN_FP8 else np.uint16) and q.ndim == 3
     T, H, D = q.shape
     if T == 0:
         return np.empty((0, H, 512)), np.empty((0, H))
@@ -156,7 +158,8 @@ def sparse_mla_fwd(q: np.ndarray, kv: np.ndarray, idx: np.ndarray,
         kv2.ctypes.data, kv_dtype, N,
         idx.ctypes.data if idx.size else None, K, ist,
         float(np.float32(sm_scale)), float(np.float32(kv_scale)), int(q_mode),
-        sk.ctypes.data if sk is not None else None, out.ctypes.data, lse.ctypes.data)
+        float(np.float32(q_scale)), sk.ctypes.data if sk is not None else None,
+        out.ctypes.data, lse.ctypes.data)
     if rc != 0:
         raise RuntimeError(f"oracle_sparse_mla_fwd failed with code {rc}")
     return out, lse

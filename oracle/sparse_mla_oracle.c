@@ -104,12 +104,13 @@ int oracle_sparse_mla_fwd(const uint16_t* q, int64_t T, int64_t H, int64_t Dqk,
                           int64_t q_stride_t, int64_t q_stride_h,
                           const void* kv, int kv_dtype, int64_t N,
                           const int32_t* idx, int64_t K, int64_t idx_stride_t,
-                          double sm_scale, double kv_scale, int q_mode,
+                          double sm_scale, double kv_scale, int q_mode, double q_scale,
                           const double* sinks, double* out, double* lse) {
   const int64_t DV = 512;
   if (T < 0 || H <= 0 || Dqk < DV || K < 0 || N < 0) return 1;
   if (kv_dtype != ORACLE_KV_BF16 && kv_dtype != ORACLE_KV_FP8_E4M3) return 2;
-  if (q_mode != ORACLE_Q_EXACT && q_mode != ORACLE_Q_TILE_FP8) return 3;
+  if (q_mode != ORACLE_Q_EXACT && q_mode != ORACLE_Q_TILE_FP8 && q_mode != ORACLE_Q_GIVEN_FP8) return 3;
+  if (q_mode == ORACLE_Q_GIVEN_FP8 && kv_dtype != ORACLE_KV_FP8_E4M3) return 3;
   if (T == 0) return 0;
 
   /* Per-tile quantised q, only for FP8 KV with FP8 dots. */
@@ -159,7 +160,9 @@ int oracle_sparse_mla_fwd(const uint16_t* q, int64_t T, int64_t H, int64_t Dqk,
           }
           /* 2. the query vector as the dots see it */
           for (int64_t d = 0; d < Dqk; ++d) {
-            if (use_q8)
+            if (q_mode == ORACLE_Q_GIVEN_FP8)
+              qhat[d] = q_scale * e4m3_table[((const uint8_t*)q)[t * q_stride_t + h * q_stride_h + d]];
+            else if (use_q8)
               qhat[d] = (double)qscales[t * G + h / 64] *
                         e4m3_table[qcodes[(t * H + h) * Dqk + d]];
             else

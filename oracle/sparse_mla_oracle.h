@@ -38,6 +38,11 @@
  *                                         magnitudes above 448 clamp to 448)
  *     qhat_d = s_q * dec(code_d)
  *
+ *   In mode ORACLE_Q_GIVEN_FP8 (fp8 KV only) q is already quantised (same first
+ *   page, Details: gfx950 keeps the pre-quantised q): the q pointer holds OCP
+ *   e4m3 codes, one byte per element with strides in bytes, and
+ *   qhat_d = q_scale * dec(code_d) with one per-tensor q_scale.
+ *
  * Parity is unpinned for nothing here: every function is pinned by the CPU
  * tests (closed forms, dense attention, library codecs).
  */
@@ -51,7 +56,7 @@ extern "C" {
 #endif
 
 enum { ORACLE_KV_BF16 = 0, ORACLE_KV_FP8_E4M3 = 1 };
-enum { ORACLE_Q_EXACT = 0, ORACLE_Q_TILE_FP8 = 1 };
+enum { ORACLE_Q_EXACT = 0, ORACLE_Q_TILE_FP8 = 1, ORACLE_Q_GIVEN_FP8 = 2 };
 
 /* bf16 bit pattern -> value (exact). */
 double oracle_bf16_value(uint16_t bits);
@@ -81,7 +86,7 @@ int oracle_sparse_mla_fwd(const uint16_t* q, int64_t T, int64_t H, int64_t Dqk,
                           int64_t q_stride_t, int64_t q_stride_h,
                           const void* kv, int kv_dtype, int64_t N,
                           const int32_t* idx, int64_t K, int64_t idx_stride_t,
-                          double sm_scale, double kv_scale, int q_mode,
+                          double sm_scale, double kv_scale, int q_mode, double q_scale,
                           const double* sinks, double* out, double* lse);
 
 /* Number of OpenMP threads the oracle will use (1 when built without it). */

@@ -22,7 +22,7 @@ DV = 512
 MAX_SPLITS = 64
 DOTS_DEFAULT = 0
 DOTS_BF16 = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_DTYPE",
                 4: "SMLA_ERR_ALIGN", 5: "SMLA_ERR_INVALID_ARG", 6: "SMLA_ERR_UNSUPPORTED",
@@ -39,7 +39,7 @@ class SparseMLAError(RuntimeError):
 class Options(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("dot_precision", ctypes.c_int32),
                 ("kernel_events", ctypes.c_void_p * 2), ("sinks", ctypes.c_void_p),
-                ("reserved", ctypes.c_int32 * 4)]
+                ("q_scale", ctypes.c_float), ("reserved", ctypes.c_int32 * 3)]
 
 
 _lib = None
@@ -138,15 +138,21 @@ def sparse_mla_fwd_ex(q: torch.Tensor, kv_pool: torch.Tensor, topk_idx: torch.Te
                       sm_scale: float, kv_scale: float = 1.0, out: torch.Tensor | None = None,
                       lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                       num_splits: int = 0, stream=None, kernel_events=None,
-                      sinks: torch.Tensor | None = None, dot_precision: int = 0):
+                      sinks: torch.Tensor | None = None, dot_precision: int = 0,
+                      q_scale: float = 0.0):
     """Sparse MLA forward; returns (out bf16 [T,H,512], lse fp32 [T,H]).
 
     kernel_events: optional pair of raw hipEvent_t handles (ints) the library
     records around its main kernel (instrumentation for benchmarks).
     sinks: optional float32 [H] per-head sink logits on q's device.
-    dot_precision: DOTS_DEFAULT or DOTS_BF16 (e4m3 KV only)."""
+    dot_precision: DOTS_DEFAULT or DOTS_BF16 (e4m3 KV only).
+    q_scale: > 0 when q is already quantised: q then holds OCP e4m3 codes (uint8 or
+    float8_e4m3fn) and qhat = q_scale * code (e4m3 KV with e4m3 dots only)."""
     lib = load_library()
-    if q.dim() != 3 or q.dtype != torch.bfloat16:
+    if q_scale > 0:
+        if q.dim() != 3 or q.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError("pre-quantised q must be uint8 / float8_e4m3fn [T, H, Dqk]")
+    elif q.dim() != 3 or q.dtype != torch.bfloat16:
         raise TypeError("q must be bfloat16 [T, H, Dqk]")
     if not q.is_cuda:
         raise ValueError("q must live on a GPU")
@@ -186,6 +192,7 @@ def sparse_mla_fwd_ex(q: torch.Tensor, kv_pool: torch.Tensor, topk_idx: torch.Te
     opts = Options()
     opts.num_splits = num_splits
     opts.dot_precision = dot_precision
+    opts.q_scale = float(q_scale)
     if sinks is not None:
         if sinks.shape != (H,) or sinks.dtype != torch.float32 or not sinks.is_contiguous():
             raise ValueError("sinks must be a contiguous float32 [H] tensor")

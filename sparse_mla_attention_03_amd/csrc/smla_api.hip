@@ -124,6 +124,7 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
     return fail(SMLA_ERR_INVALID_ARG, "sm_scale and kv_scale must be finite");
   int32_t req = 0;
   bool bf16_dots = false;
+  float q_scale = 0.0f;   // > 0: q holds e4m3 codes
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (opts) {
     if (opts->dot_precision != SMLA_DOTS_DEFAULT && opts->dot_precision != SMLA_DOTS_BF16)
@@ -131,10 +132,15 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
     if (opts->dot_precision == SMLA_DOTS_BF16 && kv_dtype != SMLA_KV_FP8_E4M3)
       return fail(SMLA_ERR_INVALID_ARG, "options.dot_precision selects bf16 dots for e4m3 KV only");
     if (opts->sinks && !aligned(opts->sinks, 4)) return fail(SMLA_ERR_ALIGN, "sinks must be 4-byte aligned");
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 3; ++i)
       if (opts->reserved[i] != 0) return fail(SMLA_ERR_INVALID_ARG, "options.reserved[%d] must be 0", i);
+    if (!(opts->q_scale == 0.0f) && !(opts->q_scale > 0.0f && std::isfinite(opts->q_scale)))
+      return fail(SMLA_ERR_INVALID_ARG, "options.q_scale must be 0 or positive and finite");
+    if (opts->q_scale > 0.0f && (kv_dtype != SMLA_KV_FP8_E4M3 || opts->dot_precision != SMLA_DOTS_DEFAULT))
+      return fail(SMLA_ERR_INVALID_ARG, "pre-quantised q (options.q_scale) needs e4m3 KV with e4m3 dots");
     req = opts->num_splits;
     bf16_dots = opts->dot_precision == SMLA_DOTS_BF16;
+    q_scale = opts->q_scale;
     ev0 = static_cast<hipEvent_t>(opts->kernel_events[0]);
     ev1 = static_cast<hipEvent_t>(opts->kernel_events[1]);
     if ((ev0 == nullptr) != (ev1 == nullptr))
@@ -147,6 +153,8 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
     return fail(SMLA_ERR_NULL, "null tensor pointer (q, kv_pool, topk_idx, out and lse are required)");
   if (!aligned(q, 16) || q_stride_t % 8 || q_stride_h % 8)
     return fail(SMLA_ERR_ALIGN, "q must be 16-byte aligned with strides that are multiples of 8 elements");
+  if (q_scale > 0.0f && (q_stride_t % 16 || q_stride_h % 16))
+    return fail(SMLA_ERR_ALIGN, "pre-quantised q needs strides that are multiples of 16 bytes");
   if (!aligned(kv_pool, 16)) return fail(SMLA_ERR_ALIGN, "kv_pool must be 16-byte aligned");
   if (!aligned(out, 16)) return fail(SMLA_ERR_ALIGN, "out must be 16-byte aligned");
   if (!aligned(lse, 4) || (topk_idx && !aligned(topk_idx, 4)))
@@ -180,6 +188,7 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;
   p.sinks = opts ? opts->sinks : nullptr;
+  p.q_scale = q_scale;
   if (plan.S > 1) {
     p.part_o = static_cast<float*>(workspace);
     p.part_lse = p.part_o + (size_t)plan.S * T * H * smla::kDV;

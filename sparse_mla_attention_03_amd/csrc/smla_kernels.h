@@ -27,6 +27,7 @@ struct FwdParams {
                                 // chunk c of the 16 heads of a group side by side
   float* part_lse;              // fp32 [S, T, H]      (S > 1)
   const float* sinks;           // fp32 [H] per-head sink logits (natural log), or null
+  float q_scale;                // > 0: q holds e4m3 codes (byte strides), qhat = q_scale * code
 };
 
 // Heads per workgroup for a head count (a multiple of 16).

@@ -189,23 +189,36 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
       qf[kb] = *reinterpret_cast<const u32x4*>(qrow + kb * 32 + 8 * g);
     c2 = p.sm_scale * p.kv_scale * kLog2e;
   } else {
-    // per-tile q quantisation: tile = heads [64*floor(h/64), +64) of token t
-    const int qt0 = (h0 / 64) * 64;
-    const int qt1 = min(qt0 + 64, p.H);
-    const float amax = q_tile_amax<DQK>(qtok, p.q_sh, qt0, qt1, s_red);
-    const float s_q = q_scale_from_amax(amax);
-    const float r_q = 1.0f / s_q;
-    // quantise this group's HT heads once, into LDS
-    constexpr int CPR = DQK / 8;
-    auto quantize_into_lds = [&](auto fast) {
-      for (int c = tid; c < HT * CPR; c += kThreads) {
-        const int hh = c / CPR, cc = c - hh * CPR;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(qtok + (int64_t)(h0 + hh) * p.q_sh + cc * 8);
-        *reinterpret_cast<u32x2*>(smem + hh * DQK + cc * 8) = quantize_chunk<decltype(fast)::value>(v, s_q, r_q);
+    float s_q;
+    if (p.q_scale > 0.0f) {
+      // q given as e4m3 codes with one per-tensor scale: copy this group's rows
+      constexpr int CPC = DQK / 16;
+      const uint8_t* qb = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)t * p.q_st;
+      for (int c = tid; c < HT * CPC; c += kThreads) {
+        const int hh = c / CPC, cc = c - hh * CPC;
+        *reinterpret_cast<u32x4*>(smem + hh * DQK + cc * 16) =
+            *reinterpret_cast<const u32x4*>(qb + (int64_t)(h0 + hh) * p.q_sh + cc * 16);
       }
-    };
-    if (q_tile_fast_div(amax)) quantize_into_lds(std::true_type{});
-    else quantize_into_lds(std::false_type{});
+      s_q = p.q_scale;
+    } else {
+      // per-tile q quantisation: tile = heads [64*floor(h/64), +64) of token t
+      const int qt0 = (h0 / 64) * 64;
+      const int qt1 = min(qt0 + 64, p.H);
+      const float amax = q_tile_amax<DQK>(qtok, p.q_sh, qt0, qt1, s_red);
+      s_q = q_scale_from_amax(amax);
+      const float r_q = 1.0f / s_q;
+      // quantise this group's HT heads once, into LDS
+      constexpr int CPR = DQK / 8;
+      auto quantize_into_lds = [&](auto fast) {
+        for (int c = tid; c < HT * CPR; c += kThreads) {
+          const int hh = c / CPR, cc = c - hh * CPR;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(qtok + (int64_t)(h0 + hh) * p.q_sh + cc * 8);
+          *reinterpret_cast<u32x2*>(smem + hh * DQK + cc * 8) = quantize_chunk<decltype(fast)::value>(v, s_q, r_q);
+        }
+      };
+      if (q_tile_fast_div(amax)) quantize_into_lds(std::true_type{});
+      else quantize_into_lds(std::false_type{});
+    }
     __syncthreads();
     const uint8_t* qs = smem + (ht * 16 + m16) * DQK;
 #pragma unroll
@@ -626,11 +639,23 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   int vidx_next2 = load_idx(1);
   constexpr int CPR = DQK / 8;                              // 16-byte chunks per head row
   constexpr int NQ = (16 * CPR + kThreads - 1) / kThreads;  // chunks per thread
+  constexpr int CPC = DQK / 16;                             // ... per row of e4m3 codes
+  constexpr int NQC = (16 * CPC + kThreads - 1) / kThreads;
+  const bool qpre = F8 && p.q_scale > 0.0f;                 // q given as e4m3 codes
   u32x4 qv[NQ];
+  if (!qpre) {
 #pragma unroll
-  for (int r = 0; r < NQ; ++r) {
-    const int c = min(tid + r * kThreads, 16 * CPR - 1), hh = c / CPR, cc = c - hh * CPR;
-    qv[r] = *reinterpret_cast<const u32x4*>(qtok + (int64_t)(h0 + hh) * p.q_sh + cc * 8);
+    for (int r = 0; r < NQ; ++r) {
+      const int c = min(tid + r * kThreads, 16 * CPR - 1), hh = c / CPR, cc = c - hh * CPR;
+      qv[r] = *reinterpret_cast<const u32x4*>(qtok + (int64_t)(h0 + hh) * p.q_sh + cc * 8);
+    }
+  } else {
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)t * p.q_st;
+#pragma unroll
+    for (int r = 0; r < NQC; ++r) {
+      const int c = min(tid + r * kThreads, 16 * CPC - 1), hh = c / CPC, cc = c - hh * CPC;
+      qv[r] = *reinterpret_cast<const u32x4*>(qb + (int64_t)(h0 + hh) * p.q_sh + cc * 16);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   u32x4 ldA[NLD];
@@ -649,6 +674,14 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
       if (c < 16 * CPR) *reinterpret_cast<u32x4*>(qs + hh * QROW + cc * 16) = qv[r];
     }
     c2 = p.sm_scale * p.kv_scale * kLog2e;
+  } else if (qpre) {
+    // codes as given, one per-tensor scale
+#pragma unroll
+    for (int r = 0; r < NQC; ++r) {
+      const int c = tid + r * kThreads, hh = c / CPC, cc = c - hh * CPC;
+      if (c < 16 * CPC) *reinterpret_cast<u32x4*>(qs + hh * QROW + cc * 16) = qv[r];
+    }
+    c2 = p.sm_scale * p.kv_scale * p.q_scale * kLog2e;
   } else {
     const int qt0 = (h0 / 64) * 64;
     const int qt1 = min(qt0 + 64, p.H);
@@ -1137,10 +1170,23 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     u32x4 qf[KV8 ? 1 : G::NKB];
     i32x8 q8[KV8 ? G::NKB : 1];
     u32x4 qv[KV8 ? G::NKB : 1][4];
+    const bool qpre = KV8 && p.q_scale > 0.0f;   // q given as e4m3 codes
     if constexpr (!KV8) {
 #pragma unroll
       for (int kb = 0; kb < G::NKB; ++kb)
         qf[kb] = *reinterpret_cast<const u32x4*>(qrow + kb * 32 + 8 * g);
+    } else if (qpre) {
+      // e4m3 codes of columns 128kb + 32g .. +32 (the B fragment as it is) in
+      // the first two chunks of the staging registers
+      const uint8_t* qb = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)t * p.q_st + (int64_t)head * p.q_sh;
+#pragma unroll
+      for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int col = 128 * kb + 32 * g + 16 * jj;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(qb + min(col, DQK - 16));
+          qv[kb][jj] = (col < DQK) ? v : u32x4{0u, 0u, 0u, 0u};
+        }
     } else {
 #pragma unroll
       for (int kb = 0; kb < G::NKB; ++kb)
@@ -1162,6 +1208,14 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     float c2;
     if constexpr (!KV8) {
       c2 = p.sm_scale * p.kv_scale * kLog2e;
+    } else if (qpre) {
+      __syncthreads();   // the output waves' barrier of the q amax exchange
+#pragma unroll
+      for (int kb = 0; kb < G::NKB; ++kb)
+        q8[kb] = i32x8{(int)qv[kb][0][0], (int)qv[kb][0][1], (int)qv[kb][0][2], (int)qv[kb][0][3],
+                       (int)qv[kb][1][0], (int)qv[kb][1][1], (int)qv[kb][1][2], (int)qv[kb][1][3]};
+      c2 = p.sm_scale * p.kv_scale * p.q_scale * kLog2e;
+      issue(ldA, vmA, vA, 0);
     } else {
       // the 64 heads are exactly one quantisation tile: amax over the four
       // score waves' registers, then s_q = amax / 448 and codes in registers

@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.sparse_mla_abi_version() == binding.ABI_VERSION == 2
+    assert lib.sparse_mla_abi_version() == binding.ABI_VERSION == 3
     seen = set()
     for st in range(9):
         s = binding.sparse_mla_status_string(st)
@@ -62,12 +62,13 @@ P = 0x7F0000000000
 
 def call(lib, q=P, T=4, H=16, D=512, qst=16 * 512, qsh=512, kv=P, dt=0, nb=16, bs=64,
          idx=P, K=128, ist=128, sm=0.04, kvs=1.0, out=P, lse=P, ws=None, wsb=0, splits=1,
-         reserved=0, events=None, dots=0, sinks=None):
+         reserved=0, events=None, dots=0, sinks=None, qsc=0.0):
     opts = binding.Options()
     opts.num_splits = splits
     opts.reserved[0] = reserved
     opts.dot_precision = dots
     opts.sinks = sinks
+    opts.q_scale = qsc
     if events:
         opts.kernel_events[0], opts.kernel_events[1] = events
     st = lib.sparse_mla_fwd_ex(q, T, H, D, qst, qsh, kv, dt, nb, bs, idx, K, ist, sm, kvs, out,
@@ -80,9 +81,10 @@ def test_empty_batch_is_a_noop(lib):
 
 
 def test_options_layout():
-    # the C struct: int32, int32, two pointers, a pointer, int32[4]
+    # the C struct: int32, int32, two pointers, a pointer, float, int32[3]
     assert ctypes.sizeof(binding.Options) == 48
-    assert binding.Options.sinks.offset == 24 and binding.Options.reserved.offset == 32
+    assert binding.Options.sinks.offset == 24 and binding.Options.q_scale.offset == 32
+    assert binding.Options.reserved.offset == 36
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -113,6 +115,12 @@ def test_options_layout():
     (dict(dots=-1), INVALID, "dot_precision"),
     (dict(dots=1), INVALID, "e4m3 KV only"),
     (dict(sinks=P + 2), ALIGN, "sinks"),
+    (dict(qsc=-1.0), INVALID, "q_scale"),
+    (dict(qsc=math.inf), INVALID, "q_scale"),
+    (dict(qsc=math.nan), INVALID, "q_scale"),
+    (dict(qsc=0.5), INVALID, "e4m3 KV with e4m3 dots"),
+    (dict(qsc=0.5, dt=1, dots=1), INVALID, "e4m3 KV with e4m3 dots"),
+    (dict(qsc=0.5, dt=1, qsh=520, qst=16 * 520), ALIGN, "multiples of 16 bytes"),
     (dict(events=(P, None)), INVALID, "kernel_events"),
     (dict(splits=2), WS, "workspace"),
     (dict(splits=2, ws=P, wsb=100), WS, "workspace"),

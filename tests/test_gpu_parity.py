@@ -434,3 +434,65 @@ def test_dot_precision_errors_match_the_pages():
     eb = rel_l2(b16.float().cpu().numpy().astype(np.float64), exact)
     assert 0.5 * lo < e8 < 1.5 * hi, e8
     assert eb < 1.5 * band["bf16_dots_rel_l2"][1], eb
+
+
+# ---------------------------------------------------------------- pre-quantised fp8 q
+
+def _prequantised_q(case):
+    """q quantised with one per-tensor scale: OCP e4m3 codes (uint8) and the scale."""
+    q = case.q.float()
+    q_scale = float(np.float32(q.abs().max().item() / 448.0))
+    codes = (q / q_scale).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    return codes, q_scale
+
+
+PREQ_CASES = [
+    # T, H, Dqk, K, ctx, pad_frac
+    (3, 16, 512, 300, 4096, 0.2),     # 16-head kernel
+    (2, 16, 576, 257, 2048, 0.1),
+    (2, 32, 512, 200, 2048, 0.0),     # 32-head kernel
+    (2, 64, 576, 190, 1024, 0.1),     # 64-head kernel
+    (2, 128, 512, 321, 4096, 0.1),
+]
+
+
+@pytest.mark.parametrize("T,H,D,K,ctx,pad", PREQ_CASES)
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_prequantised_q_parity(T, H, D, K, ctx, pad, splits):
+    case = gpu_case(T=T, H=H, Dqk=D, K=K, ctx=ctx, kv_dtype="fp8", block_size=64, seed=7 * T + H + D)
+    idx = case.topk_idx
+    if pad > 0:
+        rng = np.random.default_rng(K + 3)
+        idx = torch.from_numpy(synth.with_padding(idx.cpu().numpy(), rng, pad)).to(DEV)
+    codes, q_scale = _prequantised_q(case)
+    out, lse = sparse_mla_fwd_ex(codes, case.kv_pool, idx, case.sm_scale, case.kv_scale,
+                                 num_splits=splits, q_scale=q_scale)
+    torch.cuda.synchronize()
+    # the oracle on the rows these tokens use, with q given as codes
+    idx_np = idx.cpu().numpy()
+    N = case.kv_pool.shape[0] * case.kv_pool.shape[1]
+    valid = (idx_np >= 0) & (idx_np < N)
+    rows = np.unique(idx_np[valid]).astype(np.int64)
+    remap = np.full(idx_np.shape, -1, dtype=np.int32)
+    remap[valid] = np.searchsorted(rows, idx_np[valid]).astype(np.int32)
+    sub = case.kv_pool.reshape(N, D)[torch.from_numpy(rows).to(DEV)].cpu()
+    ref_out, ref_lse = oracle.sparse_mla_fwd(codes.cpu().numpy(), codes8(sub), remap, case.sm_scale,
+                                             case.kv_scale, q_mode=oracle.Q_GIVEN_FP8, q_scale=q_scale)
+    compare(out, lse, ref_out, ref_lse, "fp8", f"pre-quantised q T{T} H{H} D{D} S{splits}")
+
+
+@pytest.mark.parametrize("H", [16, 32, 64])
+@pytest.mark.parametrize("D", [512, 576])
+def test_prequantised_q_from_the_quantiser_is_bitwise_the_default_path(H, D):
+    # one token, H <= 64: one quantisation tile, so its codes and scale as
+    # pre-quantised q must reproduce the default (in-kernel quantisation) path
+    case = gpu_case(T=1, H=H, Dqk=D, K=300, ctx=2048, kv_dtype="fp8", seed=H + D)
+    codes, scales = binding.sparse_mla_quantize_q_fp8(case.q)
+    torch.cuda.synchronize()
+    for splits in (1, 0):
+        a = run(case, num_splits=splits)
+        b = sparse_mla_fwd_ex(codes, case.kv_pool, case.topk_idx, case.sm_scale, case.kv_scale,
+                              num_splits=splits, q_scale=float(scales[0, 0].item()))
+        torch.cuda.synchronize()
+        assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)), splits
+        assert torch.equal(a[1], b[1]), splits

@@ -21,7 +21,7 @@ import torch.nn.functional as F
 
 import oracle
 from sparse_mla_attention_03_amd import synth
-from tests.helpers import bits16, kv_bits, kv_values_f64, read_golden, rel_l2
+from tests.helpers import bits16, codes8, kv_bits, kv_values_f64, read_golden, rel_l2
 
 
 
@@ -397,3 +397,40 @@ def test_sinks_of_minus_infinity_change_nothing():
     out1, lse1 = oracle.sparse_mla_fwd(bits16(case.q), kv_bits(case.kv_pool), idx, case.sm_scale,
                                        case.kv_scale, sinks=np.full(16, -np.inf, np.float32))
     assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+
+
+# ---------------------------------------------------------------- pre-quantised fp8 q
+
+def _random_codes(shape, seed):
+    """Random finite OCP e4m3 codes (no NaN encodings 0x7f / 0xff)."""
+    c = np.random.default_rng(seed).integers(0, 256, size=shape, dtype=np.uint8)
+    return np.where((c & 0x7F) == 0x7F, c ^ 0x01, c).astype(np.uint8)
+
+
+@pytest.mark.parametrize("H,D", [(16, 512), (64, 576)])
+def test_given_codes_equal_the_per_tile_path_for_one_tile(H, D):
+    # one token with H <= 64 is one quantisation tile: its codes and scale, passed
+    # as pre-quantised q, must give the per-tile path's result exactly
+    case = _case(T=1, H=H, D=D, K=64, ctx=512, kv_dtype="fp8", seed=31)
+    codes, scales = oracle.quantize_q(bits16(case.q))
+    out_t, lse_t = _fwd(case, mode=oracle.Q_TILE_FP8)
+    out_g, lse_g = oracle.sparse_mla_fwd(codes, codes8(case.kv_pool), case.topk_idx.numpy(),
+                                         case.sm_scale, case.kv_scale, q_mode=oracle.Q_GIVEN_FP8,
+                                         q_scale=float(scales[0, 0]))
+    assert np.array_equal(out_t, out_g) and np.array_equal(lse_t, lse_g)
+
+
+def test_given_codes_full_coverage_equals_dense():
+    case = _case(T=2, H=16, D=512, ctx=256, kv_dtype="fp8", seed=33)
+    N = case.spec.N
+    idx = np.stack([np.random.default_rng(t).permutation(N) for t in range(2)]).astype(np.int32)
+    codes = _random_codes((2, 16, 512), 34)
+    q_scale = 0.0123
+    out, lse = oracle.sparse_mla_fwd(codes, codes8(case.kv_pool), idx, case.sm_scale,
+                                     case.kv_scale, q_mode=oracle.Q_GIVEN_FP8, q_scale=q_scale)
+    qhat = (torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+            * float(np.float32(q_scale)))
+    ref_out, ref_lse = dense_reference(qhat, kv_values_f64(case.kv_pool, case.kv_scale),
+                                       case.sm_scale)
+    assert np.max(np.abs(out - ref_out)) < 1e-12
+    assert np.max(np.abs(lse - ref_lse)) < 1e-12
