@@ -210,6 +210,77 @@ def cpu_baseline(cases, budget_s: float):
             "us_per_call": round(t_total / n_calls * 1e6, 1)}
 
 
+# The fused q-RoPE / q-concat / KV-concat / cache write (the step in front of the
+# forward pass), e4m3 q and cache: a decode batch of the 128-head RoPE model and
+# one 8192-token sequence of the 16-head model.  (tokens, heads, cache slots)
+ROPE_CACHE_WORKLOADS = {"rope_cache_decode": (64, 128, 64 * 32768),
+                        "rope_cache_prefill": (8192, 16, 8192)}
+
+
+def rope_cache_bench(args) -> None:
+    """One JSON line: bytes the fused op must move per call (inputs read once,
+    outputs written once) / time, against the HBM peak."""
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_03_amd import synth
+    from sparse_mla_attention_03_amd.binding import sparse_mla_rope_concat_cache
+
+    T, H, N = ROPE_CACHE_WORKLOADS[args.workload]
+    bs = 64
+    case = synth.make_rope_case(T, H, N // bs, bs, max_pos=32768, seed=6)
+    dev = torch.device("cuda:0")
+    g = [t.to(dev) for t in (case.ql_nope, case.q_pe, case.kv_c, case.k_pe, case.positions,
+                             case.cos_sin, case.slot_mapping)]
+    cache = torch.zeros((N // bs, bs, 576), dtype=torch.uint8, device=dev)
+    q_out = torch.empty((T, H, 576), dtype=torch.uint8, device=dev)
+
+    def call():
+        sparse_mla_rope_concat_cache(*g[:6], True, g[6], cache, q_out=q_out, q_fp8=True,
+                                     q_scale=0.02, kv_scale=0.011)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            call()
+    graph.replay()
+    torch.cuda.synchronize()
+    batch_ms = []
+    for _ in range(BATCHES):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        batch_ms.append(t0.elapsed_time(t1))
+    ms = float(np.median(batch_ms)) / args.steps
+    # per token: ql_nope and q_pe (bf16), kv_c and k_pe (bf16), cos/sin row (fp32),
+    # position and slot (int64) read; q_out and the cache row (e4m3) written
+    per_tok = H * (512 + 64) * 2 + (512 + 64) * 2 + 64 * 4 + 16 + H * 576 + 576
+    gbs = T * per_tok / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "fused q-RoPE + q-concat + KV-cache write, algorithmic GB/s (1 MI355X)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "us_per_call": round(ms * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "heads": H, "bytes_per_call": T * per_tok},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "batch_ms": [round(b, 4) for b in batch_ms]}), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic_summary:
@@ -223,6 +294,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
+        return
+    if args.workload in ROPE_CACHE_WORKLOADS:
+        rope_cache_bench(args)
         return
 
     import numpy as np

@@ -177,6 +177,53 @@ smla_status_t sparse_mla_quantize_q_fp8(const void* q, int64_t T, int64_t H, int
                                         int64_t q_stride_t, int64_t q_stride_h,
                                         uint8_t* codes, float* scales, void* stream);
 
+/*
+ * sparse_mla_rope_concat_cache -- the step in front of the forward pass, fused
+ * into one kernel (vLLM PR "[ROCm][MLA][Perf] Fuse decode QK-RoPE + Q-concat +
+ * KV-concat + KV-cache write for sparse MLA", Summary and Test plan): it turns
+ * a layer's absorbed query and new latent KV into the q and the cache rows the
+ * forward pass reads.  For every token t and head h:
+ *   q_out[t, h, 0:512]   = ql_nope[t, h, :]
+ *   q_out[t, h, 512:576] = RoPE(q_pe[t, h, :], positions[t])
+ *   cache row slot_mapping[t]: [0:512] = kv_c[t, :], [512:576] = RoPE(k_pe[t, :], positions[t])
+ * RoPE rotates the 64 rope columns in pairs with cos_i = cos_sin_cache[p, i],
+ * sin_i = cos_sin_cache[p, 32 + i] (i < 32):
+ *   is_neox != 0: pairs (i, i + 32) ("rotate halves");  is_neox == 0: pairs (2i, 2i + 1)
+ *   (x, y) -> (x cos_i - y sin_i, y cos_i + x sin_i)
+ * evaluated in fp64 and rounded once to bf16 (nearest even).  Encodings: a bf16
+ * output holds that bf16 value; an e4m3 output holds the OCP e4m3 code of
+ * value / scale (IEEE fp32 division, magnitudes above 448 saturate to 448,
+ * nearest even), with q_scale for q_out and kv_scale for the cache (the
+ * scaled-quantisation convention the page's tests check, with non-unit scales).
+ *
+ *   ql_nope       bf16 [T, H, 512], element (t,h,d) at ql_nope[t*ql_stride_t + h*ql_stride_h + d];
+ *                 strided (non-packed) input is read correctly.  q_pe bf16 [T, H, 64] likewise.
+ *   kv_c, k_pe    bf16 [T, 512] and [T, 64] with row strides kvc_stride_t, kpe_stride_t.
+ *                 Every row of these four inputs must be 16-byte aligned (pointer
+ *                 16-byte aligned, strides multiples of 8 elements).
+ *   positions     int64 [T]; values outside [0, max_pos) are clamped into it.
+ *   cos_sin_cache fp32 [max_pos, 64] packed, 16-byte aligned.
+ *   T, H          tokens and heads (H >= 1; T == 0 is a no-op).
+ *   q_out         [T, H, 576] packed, 16-byte aligned: bf16 (q_out_dtype 0) or e4m3 codes (1).
+ *   slot_mapping  int64 [T]: the flat cache slot of token t's row; a slot outside
+ *                 [0, num_blocks*block_size) writes nothing (e.g. -1 for padding tokens).
+ *   kv_cache      [num_blocks, block_size, 576] packed, 16-byte aligned, in kv_dtype
+ *                 (SMLA_KV_BF16 / SMLA_KV_FP8_E4M3): the pool sparse_mla_fwd reads.
+ *   q_scale, kv_scale  positive finite; used only for e4m3 outputs.
+ * Two tokens that map to one slot race (one of them wins).  Errors as for
+ * sparse_mla_fwd: checked before any launch, nothing written on error.
+ */
+smla_status_t sparse_mla_rope_concat_cache(const void* ql_nope, int64_t ql_stride_t, int64_t ql_stride_h,
+                                           const void* q_pe, int64_t qpe_stride_t, int64_t qpe_stride_h,
+                                           const void* kv_c, int64_t kvc_stride_t,
+                                           const void* k_pe, int64_t kpe_stride_t,
+                                           const int64_t* positions, const float* cos_sin_cache,
+                                           int64_t max_pos, int32_t is_neox, int64_t T, int64_t H,
+                                           void* q_out, int32_t q_out_dtype, float q_scale,
+                                           const int64_t* slot_mapping, void* kv_cache, int32_t kv_dtype,
+                                           int64_t num_blocks, int64_t block_size, float kv_scale,
+                                           void* stream);
+
 /* Static description of a status code. */
 const char* sparse_mla_status_string(smla_status_t status);
 

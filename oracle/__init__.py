@@ -68,6 +68,13 @@ def _load():
         c_p, c_i64, c_i64,
         ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_double,
         c_p, c_p, c_p]
+    lib.oracle_bf16_round.restype = ctypes.c_uint16
+    lib.oracle_bf16_round.argtypes = [ctypes.c_double]
+    lib.oracle_rope_concat_cache.restype = ctypes.c_int
+    lib.oracle_rope_concat_cache.argtypes = [
+        c_p, c_i64, c_i64, c_p, c_i64, c_i64, c_p, c_i64, c_p, c_i64,
+        c_p, c_p, c_i64, ctypes.c_int, c_i64, c_i64,
+        c_p, ctypes.c_int, ctypes.c_double, c_p, c_p, ctypes.c_int, c_i64, ctypes.c_double]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -163,3 +170,39 @@ def sparse_mla_fwd(q: np.ndarray, kv: np.ndarray, idx: np.ndarray,
     if rc != 0:
         raise RuntimeError(f"oracle_sparse_mla_fwd failed with code {rc}")
     return out, lse
+
+
+def bf16_round(v: float) -> int:
+    """Nearest bf16 (bits) to the real number v, ties to even."""
+    return int(_load().oracle_bf16_round(float(v)))
+
+
+def rope_concat_cache(ql_nope: np.ndarray, q_pe: np.ndarray, kv_c: np.ndarray, k_pe: np.ndarray,
+                      positions: np.ndarray, cos_sin: np.ndarray, is_neox: bool,
+                      slot_mapping: np.ndarray, kv_cache: np.ndarray, q_fp8: bool = False,
+                      q_scale: float = 1.0, kv_scale: float = 1.0):
+    """The fused q-RoPE / concat / cache write.  bf16 inputs as uint16 bits (any
+    strides, last axis contiguous); kv_cache [N, 576] of uint16 (bf16) or uint8
+    (e4m3) is copied and the copy written.  Returns (q_out [T, H, 576] uint16 or
+    uint8, kv_cache_out).  Scales are rounded to fp32 as the library receives them."""
+    lib = _load()
+    T, H, D = ql_nope.shape
+    assert D == 512 and q_pe.shape == (T, H, 64) and kv_c.shape == (T, 512) and k_pe.shape == (T, 64)
+    for a in (ql_nope, q_pe, kv_c, k_pe):
+        assert a.dtype == np.uint16 and a.strides[-1] == 2
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    cs = np.ascontiguousarray(cos_sin, dtype=np.float32)
+    assert cs.ndim == 2 and cs.shape[1] == 64
+    cache = np.array(kv_cache.reshape(-1, 576), copy=True, order="C")
+    kv_fp8 = cache.dtype == np.uint8
+    q_out = np.zeros((T, H, 576), dtype=np.uint8 if q_fp8 else np.uint16)
+    rc = lib.oracle_rope_concat_cache(
+        ql_nope.ctypes.data, *_strides_elems(ql_nope)[:2], q_pe.ctypes.data, *_strides_elems(q_pe)[:2],
+        kv_c.ctypes.data, _strides_elems(kv_c)[0], k_pe.ctypes.data, _strides_elems(k_pe)[0],
+        pos.ctypes.data, cs.ctypes.data, cs.shape[0], int(bool(is_neox)), T, H,
+        q_out.ctypes.data, int(bool(q_fp8)), float(np.float32(q_scale)),
+        slots.ctypes.data, cache.ctypes.data, int(kv_fp8), cache.shape[0], float(np.float32(kv_scale)))
+    if rc != 0:
+        raise RuntimeError(f"oracle_rope_concat_cache failed with code {rc}")
+    return q_out, cache.reshape(kv_cache.shape)

@@ -209,3 +209,84 @@ int oracle_sparse_mla_fwd(const uint16_t* q, int64_t T, int64_t H, int64_t Dqk,
   free(qscales);
   return failed ? 5 : 0;
 }
+
+/* ---- the fused q-RoPE / q-concat / KV-concat / cache write --------------- */
+
+/* Nearest bf16 to a real number v (given exactly as a double), ties to even:
+ * bf16 keeps 8 significant bits with the binary32 exponent range, so the
+ * spacing near |v| in [2^(e-1), 2^e) is 2^(e-8), and 2^-133 below the
+ * smallest normal 2^-126. */
+uint16_t oracle_bf16_round(double v) {
+  if (isnan(v)) return 0x7FC0;
+  uint16_t sign = signbit(v) ? 0x8000 : 0x0000;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);
+  int qexp = e - 8;
+  if (qexp < -133) qexp = -133;
+  double r = ldexp(nearbyint(ldexp(a, -qexp)), qexp);   /* ties to even */
+  if (r > 3.3895313892515355e38) return sign | 0x7F80;  /* beyond the largest bf16: inf */
+  float f = (float)r;                                   /* exact: r is a bf16 number */
+  uint32_t w;
+  memcpy(&w, &f, sizeof w);
+  return sign | (uint16_t)((w >> 16) & 0x7FFF);
+}
+
+/* RoPE of one 64-column bf16 row at one position, as bf16 bits.  Pairs are
+ * (i, i + 32) for the rotate-halves ("neox") form and (2i, 2i + 1) for the
+ * interleaved form; pair i turns by the angle whose cosine / sine are
+ * cs[i] / cs[32 + i]: (x, y) -> (x cos - y sin, y cos + x sin), formed in fp64
+ * (both products exact) and rounded once to bf16. */
+static void rope_row(const uint16_t* x, const float* cs, int is_neox, uint16_t* out) {
+  for (int i = 0; i < 32; ++i) {
+    const int ix = is_neox ? i : 2 * i;
+    const int iy = is_neox ? i + 32 : 2 * i + 1;
+    const double c = cs[i], s = cs[32 + i];
+    const double xv = oracle_bf16_value(x[ix]), yv = oracle_bf16_value(x[iy]);
+    out[ix] = oracle_bf16_round(xv * c - yv * s);
+    out[iy] = oracle_bf16_round(yv * c + xv * s);
+  }
+}
+
+/* one output element: bf16 bits as they are, or the e4m3 code of value / scale
+ * (the quotient rounded to binary32 first) */
+static void put(void* base, int64_t i, int fp8, double scale, uint16_t bits) {
+  if (fp8) {
+    float qf = (float)(oracle_bf16_value(bits) / scale);
+    ((uint8_t*)base)[i] = oracle_e4m3_encode_rne_sat(qf);
+  } else {
+    ((uint16_t*)base)[i] = bits;
+  }
+}
+
+int oracle_rope_concat_cache(const uint16_t* ql_nope, int64_t ql_st, int64_t ql_sh,
+                             const uint16_t* q_pe, int64_t qpe_st, int64_t qpe_sh,
+                             const uint16_t* kv_c, int64_t kvc_st,
+                             const uint16_t* k_pe, int64_t kpe_st,
+                             const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                             int is_neox, int64_t T, int64_t H,
+                             void* q_out, int q_fp8, double q_scale,
+                             const int64_t* slot_mapping, void* kv_cache, int kv_fp8, int64_t N,
+                             double kv_scale) {
+  if (T < 0 || H <= 0 || max_pos <= 0 || N < 0) return 1;
+  uint16_t rot[64];
+  for (int64_t t = 0; t < T; ++t) {
+    int64_t p = positions[t];
+    if (p < 0) p = 0;
+    if (p >= max_pos) p = max_pos - 1;
+    const float* cs = cos_sin + p * 64;
+    for (int64_t h = 0; h < H; ++h) {
+      const int64_t o = (t * H + h) * 576;
+      for (int d = 0; d < 512; ++d) put(q_out, o + d, q_fp8, q_scale, ql_nope[t * ql_st + h * ql_sh + d]);
+      rope_row(q_pe + t * qpe_st + h * qpe_sh, cs, is_neox, rot);
+      for (int d = 0; d < 64; ++d) put(q_out, o + 512 + d, q_fp8, q_scale, rot[d]);
+    }
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= N) continue;
+    for (int d = 0; d < 512; ++d) put(kv_cache, slot * 576 + d, kv_fp8, kv_scale, kv_c[t * kvc_st + d]);
+    rope_row(k_pe + t * kpe_st, cs, is_neox, rot);
+    for (int d = 0; d < 64; ++d) put(kv_cache, slot * 576 + 512 + d, kv_fp8, kv_scale, rot[d]);
+  }
+  return 0;
+}

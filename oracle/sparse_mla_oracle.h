@@ -89,6 +89,31 @@ int oracle_sparse_mla_fwd(const uint16_t* q, int64_t T, int64_t H, int64_t Dqk,
                           double sm_scale, double kv_scale, int q_mode, double q_scale,
                           const double* sinks, double* out, double* lse);
 
+/* Nearest bf16 (bits) to a real number given exactly as a double, ties to even. */
+uint16_t oracle_bf16_round(double v);
+
+/* The fused q-RoPE / q-concat / KV-concat / cache write, element by element
+ * (vLLM PR "[ROCm][MLA][Perf] Fuse decode QK-RoPE + Q-concat + KV-concat +
+ * KV-cache write for sparse MLA", Summary and Test plan):
+ *   q_out[t,h] = concat(ql_nope[t,h], RoPE(q_pe[t,h], positions[t]))   [576]
+ *   cache row slot_mapping[t] = concat(kv_c[t], RoPE(k_pe[t], positions[t]))
+ * RoPE: 32 pairs, (i, i+32) when is_neox else (2i, 2i+1); pair i turns by the
+ * angle with cosine cos_sin[p*64 + i] and sine cos_sin[p*64 + 32 + i]; each
+ * result is the exact x cos - y sin / y cos + x sin rounded once to bf16.
+ * Positions are clamped into [0, max_pos); slots outside [0, N) write nothing.
+ * Outputs: bf16 bits, or (q_fp8 / kv_fp8) the e4m3 code of value / scale with
+ * the quotient rounded to binary32, saturated at 448, nearest even.
+ * Strides in elements.  Returns 0, or nonzero on bad sizes. */
+int oracle_rope_concat_cache(const uint16_t* ql_nope, int64_t ql_st, int64_t ql_sh,
+                             const uint16_t* q_pe, int64_t qpe_st, int64_t qpe_sh,
+                             const uint16_t* kv_c, int64_t kvc_st,
+                             const uint16_t* k_pe, int64_t kpe_st,
+                             const int64_t* positions, const float* cos_sin, int64_t max_pos,
+                             int is_neox, int64_t T, int64_t H,
+                             void* q_out, int q_fp8, double q_scale,
+                             const int64_t* slot_mapping, void* kv_cache, int kv_fp8, int64_t N,
+                             double kv_scale);
+
 /* Number of OpenMP threads the oracle will use (1 when built without it). */
 int oracle_num_threads(void);
 

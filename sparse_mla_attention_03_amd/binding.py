@@ -72,6 +72,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sparse_mla_status_string.restype = ctypes.c_char_p
     lib.sparse_mla_last_error.argtypes = []
     lib.sparse_mla_last_error.restype = ctypes.c_char_p
+    lib.sparse_mla_rope_concat_cache.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, vp, i64, vp, vp, i64, i32,
+                                                  i64, i64, vp, i32, f32, vp, vp, i32, i64, i64, f32, vp]
+    lib.sparse_mla_rope_concat_cache.restype = ctypes.c_int
     lib.sparse_mla_abi_version.argtypes = []
     lib.sparse_mla_abi_version.restype = i32
     if path is None:
@@ -237,3 +240,55 @@ def sparse_mla_quantize_q_fp8(q: torch.Tensor, codes: torch.Tensor | None = None
                                        scales.data_ptr(), _stream_handle(q.device, stream))
     _check(st)
     return codes, scales
+
+
+def sparse_mla_rope_concat_cache(ql_nope: torch.Tensor, q_pe: torch.Tensor, kv_c: torch.Tensor,
+                                 k_pe: torch.Tensor, positions: torch.Tensor,
+                                 cos_sin_cache: torch.Tensor, is_neox: bool,
+                                 slot_mapping: torch.Tensor, kv_cache: torch.Tensor,
+                                 q_out: torch.Tensor | None = None, q_fp8: bool = False,
+                                 q_scale: float = 1.0, kv_scale: float = 1.0, stream=None):
+    """Fused q-RoPE + q-concat + KV-concat + cache write; returns q_out [T, H, 576]
+    (bf16, or e4m3 codes as uint8 when q_fp8).  kv_cache [num_blocks, block_size, 576]
+    (bf16, or uint8 / float8_e4m3fn codes) is written in place."""
+    lib = load_library()
+    if ql_nope.dim() != 3 or ql_nope.dtype != torch.bfloat16 or ql_nope.shape[2] != DV:
+        raise TypeError("ql_nope must be bfloat16 [T, H, 512]")
+    T, H, _ = ql_nope.shape
+    if q_pe.shape != (T, H, 64) or q_pe.dtype != torch.bfloat16:
+        raise TypeError("q_pe must be bfloat16 [T, H, 64]")
+    if kv_c.shape != (T, DV) or kv_c.dtype != torch.bfloat16 or k_pe.shape != (T, 64) or k_pe.dtype != torch.bfloat16:
+        raise TypeError("kv_c / k_pe must be bfloat16 [T, 512] / [T, 64]")
+    for x, name in ((ql_nope, "ql_nope"), (q_pe, "q_pe")):
+        if T > 0 and x.stride(2) != 1:
+            raise ValueError(f"{name}'s last dimension must be contiguous")
+    for x, name in ((kv_c, "kv_c"), (k_pe, "k_pe")):
+        if T > 0 and x.stride(1) != 1:
+            raise ValueError(f"{name}'s last dimension must be contiguous")
+    if positions.shape != (T,) or positions.dtype != torch.int64 or slot_mapping.shape != (T,) \
+            or slot_mapping.dtype != torch.int64:
+        raise TypeError("positions and slot_mapping must be int64 [T]")
+    if cos_sin_cache.dim() != 2 or cos_sin_cache.shape[1] != 64 or cos_sin_cache.dtype != torch.float32 \
+            or not cos_sin_cache.is_contiguous():
+        raise TypeError("cos_sin_cache must be a contiguous float32 [max_pos, 64] tensor")
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != 576 or not kv_cache.is_contiguous():
+        raise TypeError("kv_cache must be a contiguous [num_blocks, block_size, 576] tensor")
+    kvd = _kv_dtype(kv_cache)
+    qdt = torch.uint8 if q_fp8 else torch.bfloat16
+    if q_out is None:
+        q_out = torch.empty((T, H, 576), dtype=qdt, device=ql_nope.device)
+    if q_out.shape != (T, H, 576) or q_out.dtype != qdt or not q_out.is_contiguous():
+        raise ValueError("q_out must be a contiguous [T, H, 576] tensor of the output dtype")
+    for x in (q_pe, kv_c, k_pe, positions, cos_sin_cache, slot_mapping, kv_cache, q_out):
+        if x.device != ql_nope.device:
+            raise ValueError("all tensors must be on one device")
+    st = lib.sparse_mla_rope_concat_cache(
+        ql_nope.data_ptr(), ql_nope.stride(0), ql_nope.stride(1),
+        q_pe.data_ptr(), q_pe.stride(0), q_pe.stride(1),
+        kv_c.data_ptr(), kv_c.stride(0), k_pe.data_ptr(), k_pe.stride(0),
+        positions.data_ptr(), cos_sin_cache.data_ptr(), cos_sin_cache.shape[0], int(bool(is_neox)),
+        T, H, q_out.data_ptr(), 1 if q_fp8 else 0, float(q_scale),
+        slot_mapping.data_ptr(), kv_cache.data_ptr(), kvd, kv_cache.shape[0], kv_cache.shape[1],
+        float(kv_scale), _stream_handle(ql_nope.device, stream))
+    _check(st)
+    return q_out

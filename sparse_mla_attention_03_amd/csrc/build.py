@@ -2,7 +2,7 @@
 
     python -m sparse_mla_attention_03_amd.csrc.build      # or build.build()
 
-The two translation units compile in parallel, then link into one shared
+The translation units compile in parallel, then link into one shared
 library exporting the C ABI of include/sparse_mla.h.
 """
 from __future__ import annotations
@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsparsemla.so")
-SOURCES = ["smla_api.hip", "smla_kernels.hip"]
+SOURCES = ["smla_api.hip", "smla_kernels.hip", "smla_rope_cache.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -273,6 +273,71 @@ smla_status_t sparse_mla_quantize_q_fp8(const void* q, int64_t T, int64_t H, int
   return SMLA_OK;
 }
 
+smla_status_t sparse_mla_rope_concat_cache(const void* ql_nope, int64_t ql_stride_t, int64_t ql_stride_h,
+                                           const void* q_pe, int64_t qpe_stride_t, int64_t qpe_stride_h,
+                                           const void* kv_c, int64_t kvc_stride_t,
+                                           const void* k_pe, int64_t kpe_stride_t,
+                                           const int64_t* positions, const float* cos_sin_cache,
+                                           int64_t max_pos, int32_t is_neox, int64_t T, int64_t H,
+                                           void* q_out, int32_t q_out_dtype, float q_scale,
+                                           const int64_t* slot_mapping, void* kv_cache, int32_t kv_dtype,
+                                           int64_t num_blocks, int64_t block_size, float kv_scale,
+                                           void* stream) {
+  g_last_error.clear();
+  if (T < 0 || H <= 0 || T > 0x7fffffff || H > 0x7fffffff || max_pos <= 0 || num_blocks < 0 || block_size <= 0)
+    return fail(SMLA_ERR_SHAPE, "bad sizes T=%lld H=%lld max_pos=%lld num_blocks=%lld block_size=%lld",
+                (long long)T, (long long)H, (long long)max_pos, (long long)num_blocks, (long long)block_size);
+  if (ql_stride_t < 0 || ql_stride_h < 0 || qpe_stride_t < 0 || qpe_stride_h < 0 || kvc_stride_t < 0 ||
+      kpe_stride_t < 0)
+    return fail(SMLA_ERR_SHAPE, "negative stride");
+  if ((q_out_dtype != SMLA_KV_BF16 && q_out_dtype != SMLA_KV_FP8_E4M3) ||
+      (kv_dtype != SMLA_KV_BF16 && kv_dtype != SMLA_KV_FP8_E4M3))
+    return fail(SMLA_ERR_DTYPE, "q_out_dtype=%d / kv_dtype=%d unknown", q_out_dtype, kv_dtype);
+  if (!(q_scale > 0.0f && std::isfinite(q_scale)) || !(kv_scale > 0.0f && std::isfinite(kv_scale)))
+    return fail(SMLA_ERR_INVALID_ARG, "q_scale and kv_scale must be positive and finite");
+  if (T * (H + 1) * 72 > 0xffffffffLL)
+    return fail(SMLA_ERR_UNSUPPORTED, "T=%lld x H=%lld is beyond one launch (T*(H+1)*72 < 2^32)",
+                (long long)T, (long long)H);
+  if (T == 0) return SMLA_OK;
+  if (!ql_nope || !q_pe || !kv_c || !k_pe || !positions || !cos_sin_cache || !q_out || !slot_mapping ||
+      !kv_cache)
+    return fail(SMLA_ERR_NULL, "null tensor pointer");
+  const bool rows_ok = aligned(ql_nope, 16) && aligned(q_pe, 16) && aligned(kv_c, 16) && aligned(k_pe, 16) &&
+                       ql_stride_t % 8 == 0 && ql_stride_h % 8 == 0 && qpe_stride_t % 8 == 0 &&
+                       qpe_stride_h % 8 == 0 && kvc_stride_t % 8 == 0 && kpe_stride_t % 8 == 0;
+  if (!rows_ok)
+    return fail(SMLA_ERR_ALIGN, "ql_nope, q_pe, kv_c and k_pe rows must be 16-byte aligned (strides multiples of 8)");
+  if (!aligned(cos_sin_cache, 16) || !aligned(q_out, 16) || !aligned(kv_cache, 16) || !aligned(positions, 8) ||
+      !aligned(slot_mapping, 8))
+    return fail(SMLA_ERR_ALIGN, "cos_sin_cache, q_out and kv_cache must be 16-byte aligned, positions and slot_mapping 8-byte");
+  smla::RopeCacheParams p{};
+  p.ql_nope = static_cast<const uint16_t*>(ql_nope);
+  p.ql_st = ql_stride_t;
+  p.ql_sh = ql_stride_h;
+  p.q_pe = static_cast<const uint16_t*>(q_pe);
+  p.qpe_st = qpe_stride_t;
+  p.qpe_sh = qpe_stride_h;
+  p.kv_c = static_cast<const uint16_t*>(kv_c);
+  p.kvc_st = kvc_stride_t;
+  p.k_pe = static_cast<const uint16_t*>(k_pe);
+  p.kpe_st = kpe_stride_t;
+  p.positions = positions;
+  p.cos_sin = cos_sin_cache;
+  p.max_pos = max_pos;
+  p.T = (int32_t)T;
+  p.H = (int32_t)H;
+  p.q_out = static_cast<uint8_t*>(q_out);
+  p.q_scale = q_scale;
+  p.slot_mapping = slot_mapping;
+  p.kv_cache = static_cast<uint8_t*>(kv_cache);
+  p.N = num_blocks * block_size;
+  p.kv_scale = kv_scale;
+  hipError_t e = smla::launch_rope_cache(p, is_neox != 0, q_out_dtype == SMLA_KV_FP8_E4M3,
+                                         kv_dtype == SMLA_KV_FP8_E4M3, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "launch: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
 const char* sparse_mla_status_string(smla_status_t status) {
   switch (status) {
     case SMLA_OK: return "ok";

@@ -30,6 +30,28 @@ struct FwdParams {
   float q_scale;                // > 0: q holds e4m3 codes (byte strides), qhat = q_scale * code
 };
 
+// The fused q-RoPE / q-concat / KV-concat / cache write (strides in elements).
+struct RopeCacheParams {
+  const uint16_t* ql_nope;      // bf16 [T, H, 512]
+  int64_t ql_st, ql_sh;
+  const uint16_t* q_pe;         // bf16 [T, H, 64]
+  int64_t qpe_st, qpe_sh;
+  const uint16_t* kv_c;         // bf16 [T, 512]
+  int64_t kvc_st;
+  const uint16_t* k_pe;         // bf16 [T, 64]
+  int64_t kpe_st;
+  const int64_t* positions;     // [T]
+  const float* cos_sin;         // fp32 [max_pos, 64]: cos 0..31, sin 32..63
+  int64_t max_pos;
+  int32_t T, H;
+  uint8_t* q_out;               // [T, H, 576] bf16 or e4m3
+  float q_scale;
+  const int64_t* slot_mapping;  // [T]
+  uint8_t* kv_cache;            // [N, 576] bf16 or e4m3
+  int64_t N;
+  float kv_scale;
+};
+
 // Heads per workgroup for a head count (a multiple of 16).
 inline int heads_per_workgroup(int64_t H) { return (H % 64 == 0) ? 64 : (H % 32 == 0) ? 32 : 16; }
 
@@ -39,6 +61,7 @@ inline int heads_per_workgroup(int64_t H) { return (H % 64 == 0) ? 64 : (H % 32 
 hipError_t launch_fwd(const FwdParams& p, bool kv_fp8, bool bf16_dots, int dqk, hipStream_t stream,
                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_combine(const FwdParams& p, hipStream_t stream);
+hipError_t launch_rope_cache(const RopeCacheParams& p, bool neox, bool q8, bool kv8, hipStream_t stream);
 hipError_t launch_quantize_q(const uint16_t* q, int64_t q_st, int64_t q_sh, int32_t T, int32_t H,
                              int dqk, uint8_t* codes, float* scales, hipStream_t stream);
 

@@ -1,0 +1,178 @@
+// smla_rope_cache.hip -- the step in front of the forward pass, fused: RoPE on the
+// 64 rope columns of q and of the new KV row, the q concat and the KV-cache
+// write (vLLM PR "[ROCm][MLA][Perf] Fuse decode QK-RoPE + Q-concat + KV-concat +
+// KV-cache write for sparse MLA", Summary and Test plan).
+//
+// Every token has H q rows (576 outputs each) and one cache row (576
+// outputs): R = T (H + 1) rows in all, row r belonging to token r / (H + 1).
+// The work is split by wave, so no wave mixes the two kinds of chunk:
+//   latent waves copy (or quantise) the 512 latent columns of kLatentRows rows,
+//     lane l taking 16-byte chunk l of each (that many 1 KB loads in flight per
+//     wave, each contiguous across the lanes);
+//   rope waves rotate the 64 rope columns of eight rows, eight lanes per row:
+//   (x, y) -> (x cos - y sin, y cos + x sin)
+// with the pairs (i, i + 32) (rotate-halves, "neox") or (2i, 2i + 1)
+// (interleaved).  The rotation is evaluated in fp64 -- both products are exact
+// for a bf16 times an fp32, so one rounding happens, at the difference -- and
+// rounded once to bf16 (through fp32 with round-to-odd, which keeps the final
+// round-to-nearest-even exact).  e4m3 outputs encode value / scale (IEEE fp32
+// division, saturated to +-448, round to nearest even) of the bf16 value.
+#include <hip/hip_runtime.h>
+
+#include "smla_device.h"
+#include "smla_kernels.h"
+
+namespace smla {
+
+namespace {
+
+constexpr int kRopeCols = 64;
+constexpr int kLatentRows = 4;   // rows per latent wave
+
+// fp64 -> bf16 bits, round to nearest even, in two steps that round once: to
+// fp32 toward zero with the sticky "inexact" bit folded into the last place
+// (round to odd), then fp32 -> bf16 to nearest even.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double d) {
+  float f = __double2float_rz(d);
+  uint32_t b = __float_as_uint(f);
+  if ((double)f != d) b |= 1u;
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+// eight outputs (as fp32 values of bf16 numbers) -> their encoding at dst
+template <bool E4M3>
+__device__ __forceinline__ void store8(uint8_t* dst, const float (&v)[8], float scale) {
+  if constexpr (!E4M3) {
+    *reinterpret_cast<u32x4*>(dst) =
+        u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
+  } else {
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(v[i] / scale, -kE4m3Max), kE4m3Max);
+    *reinterpret_cast<u32x2*>(dst) =
+        u32x2{f32x4_to_e4m3x4(y[0], y[1], y[2], y[3]), f32x4_to_e4m3x4(y[4], y[5], y[6], y[7])};
+  }
+}
+
+__device__ __forceinline__ void unpack8(const u32x4& w, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_lo(w[i]);
+    v[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+// chunk j (rope columns 8j .. 8j+7) of RoPE(x) for one 64-column bf16 row x
+template <bool NEOX>
+__device__ __forceinline__ void rope8(const uint16_t* x, const float* cs, int j, float (&v)[8]) {
+  float own[8];
+  unpack8(*reinterpret_cast<const u32x4*>(x + 8 * j), own);
+  if constexpr (NEOX) {
+    // column i pairs with i ^ 32; both halves use frequency i mod 32
+    float other[8];
+    unpack8(*reinterpret_cast<const u32x4*>(x + 8 * (j ^ 4)), other);
+    const int f0 = 8 * (j & 3);
+    const bool first = j < 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double c = cs[f0 + i], s = cs[32 + f0 + i];
+      const double a = own[i], b = other[i];
+      v[i] = __uint_as_float(f64_to_bf16_rne(first ? a * c - b * s : a * c + b * s) << 16);
+    }
+  } else {
+    // pairs (2m, 2m + 1), frequency m
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * j + i;
+      const double c = cs[m], s = cs[32 + m];
+      const double a = own[2 * i], b = own[2 * i + 1];
+      v[2 * i] = __uint_as_float(f64_to_bf16_rne(a * c - b * s) << 16);
+      v[2 * i + 1] = __uint_as_float(f64_to_bf16_rne(b * c + a * s) << 16);
+    }
+  }
+}
+
+// destination of output column 8k of row r, or null when the row is a cache
+// row whose slot is out of range
+template <bool Q8, bool KV8>
+__device__ __forceinline__ uint8_t* row_dst(const RopeCacheParams& p, int t, int h, int k) {
+  if (h < p.H) return p.q_out + (((int64_t)t * p.H + h) * (kDV + kRopeCols) + 8 * k) * (Q8 ? 1 : 2);
+  const int64_t slot = p.slot_mapping[t];
+  if (slot < 0 || slot >= p.N) return nullptr;
+  return p.kv_cache + (slot * (kDV + kRopeCols) + 8 * k) * (KV8 ? 1 : 2);
+}
+
+template <bool NEOX, bool Q8, bool KV8>
+__global__ __launch_bounds__(kThreads) void smla_rope_cache_kernel(RopeCacheParams p, uint32_t latent_waves) {
+  const uint32_t w = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const uint32_t rows = (uint32_t)p.H + 1;
+  const uint32_t R = (uint32_t)p.T * rows;
+  if (w < latent_waves) {
+    // ---- latent columns of rows LW w .. LW w + LW - 1, lane = 16-byte chunk
+    constexpr int LW = kLatentRows;
+    float v[LW][8];
+    int tt[LW], hh[LW];
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+      const uint32_t r = min(LW * w + i, R - 1);   // clamped; rows past R are not stored
+      tt[i] = (int)(r / rows);
+      hh[i] = (int)(r - (uint32_t)tt[i] * rows);
+      const uint16_t* src = (hh[i] < p.H) ? p.ql_nope + tt[i] * p.ql_st + hh[i] * p.ql_sh
+                                          : p.kv_c + tt[i] * p.kvc_st;
+      unpack8(*reinterpret_cast<const u32x4*>(src + 8 * lane), v[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+      if (LW * w + i >= R) break;
+      if (hh[i] < p.H) {
+        store8<Q8>(row_dst<Q8, KV8>(p, tt[i], hh[i], lane), v[i], p.q_scale);
+      } else {
+        uint8_t* d = row_dst<Q8, KV8>(p, tt[i], hh[i], lane);
+        if (d) store8<KV8>(d, v[i], p.kv_scale);
+      }
+    }
+  } else {
+    // ---- rope columns of rows 8w' .. 8w' + 7, eight lanes per row
+    const uint32_t r = (w - latent_waves) * 8 + (lane >> 3);
+    if (r >= R) return;
+    const int j = lane & 7;
+    const int t = (int)(r / rows);
+    const int h = (int)(r - (uint32_t)t * rows);
+    const int64_t pos = min(max(p.positions[t], (int64_t)0), p.max_pos - 1);
+    const float* cs = p.cos_sin + pos * kRopeCols;
+    float v[8];
+    if (h < p.H) {
+      rope8<NEOX>(p.q_pe + t * p.qpe_st + h * p.qpe_sh, cs, j, v);
+      store8<Q8>(row_dst<Q8, KV8>(p, t, h, kDV / 8 + j), v, p.q_scale);
+    } else {
+      uint8_t* d = row_dst<Q8, KV8>(p, t, h, kDV / 8 + j);
+      if (d == nullptr) return;
+      rope8<NEOX>(p.k_pe + t * p.kpe_st, cs, j, v);
+      store8<KV8>(d, v, p.kv_scale);
+    }
+  }
+}
+
+template <bool NEOX, bool Q8>
+hipError_t launch_rc2(const RopeCacheParams& p, bool kv8, hipStream_t stream) {
+  const int64_t R = (int64_t)p.T * (p.H + 1);
+  const uint32_t latent_waves = (uint32_t)((R + kLatentRows - 1) / kLatentRows);
+  const int64_t waves = latent_waves + (R + 7) / 8;
+  const dim3 gd((unsigned)((waves + 3) / 4)), bd(kThreads);
+  if (kv8)
+    hipLaunchKernelGGL((smla_rope_cache_kernel<NEOX, Q8, true>), gd, bd, 0, stream, p, latent_waves);
+  else
+    hipLaunchKernelGGL((smla_rope_cache_kernel<NEOX, Q8, false>), gd, bd, 0, stream, p, latent_waves);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rope_cache(const RopeCacheParams& p, bool neox, bool q8, bool kv8, hipStream_t stream) {
+  if (neox) return q8 ? launch_rc2<true, true>(p, kv8, stream) : launch_rc2<true, false>(p, kv8, stream);
+  return q8 ? launch_rc2<false, true>(p, kv8, stream) : launch_rc2<false, false>(p, kv8, stream);
+}
+
+}  // namespace smla

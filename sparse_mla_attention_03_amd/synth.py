@@ -212,6 +212,46 @@ def with_padding(idx: np.ndarray, rng: np.random.Generator, frac: float) -> np.n
     return out
 
 
-__all__ = ["Spec", "Case", "CONFIGS", "make_case", "make_pool", "small_spec", "topk_slots",
+def rope_cos_sin(max_pos: int, base: float = 10000.0) -> np.ndarray:
+    """A rotary table in the usual layout: [max_pos, 64] fp32, cosines of the 32
+    pair angles pos * base^(-2i/64) in columns 0..31, sines in 32..63."""
+    inv = base ** (-np.arange(0, 64, 2, dtype=np.float64) / 64.0)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+@dataclass
+class RopeCase:
+    ql_nope: torch.Tensor     # bf16 [T, H, 512]
+    q_pe: torch.Tensor        # bf16 [T, H, 64]
+    kv_c: torch.Tensor        # bf16 [T, 512]
+    k_pe: torch.Tensor        # bf16 [T, 64]
+    positions: torch.Tensor   # int64 [T]
+    cos_sin: torch.Tensor     # fp32 [max_pos, 64]
+    slot_mapping: torch.Tensor  # int64 [T], -1 = no cache write
+    num_blocks: int
+    block_size: int
+
+
+def make_rope_case(T: int, H: int, num_blocks: int, block_size: int, max_pos: int = 8192,
+                   seed: int = 0, skip_frac: float = 0.0, device: str = "cpu") -> RopeCase:
+    """Seeded inputs of the fused q-RoPE / cache write: N(0,1) activations,
+    random positions, distinct random cache slots (a fraction set to -1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    def bf(shape):
+        return torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(torch.bfloat16)
+    ql, qp, kc, kp = bf((T, H, 512)), bf((T, H, 64)), bf((T, 512)), bf((T, 64))
+    pos = rng.integers(0, max_pos, size=T).astype(np.int64)
+    N = num_blocks * block_size
+    slots = rng.choice(N, size=T, replace=False).astype(np.int64)
+    if skip_frac > 0:
+        slots[rng.random(T) < skip_frac] = -1
+    dev = torch.device(device)
+    return RopeCase(ql.to(dev), qp.to(dev), kc.to(dev), kp.to(dev), torch.from_numpy(pos).to(dev),
+                    torch.from_numpy(rope_cos_sin(max_pos)).to(dev), torch.from_numpy(slots).to(dev),
+                    num_blocks, block_size)
+
+
+__all__ = ["RopeCase", "make_rope_case", "rope_cos_sin", "Spec", "Case", "CONFIGS", "make_case", "make_pool", "small_spec", "topk_slots",
            "topk_positions", "block_table", "positions_to_slots", "quantize_e4m3",
            "with_padding", "E4M3_MAX", "replace"]

@@ -1,0 +1,114 @@
+"""GPU parity of the fused q-RoPE / q-concat / KV-concat / cache write against the
+fp64 oracle: bit for bit (every output is a bf16 pattern or an e4m3 code that
+both sides decide from the same exactly-rounded value), for both pair layouts,
+16 and 128 heads, block sizes 1 and 64, bf16 and e4m3 outputs with non-unit
+scales, skipped slots and a strided (heads-outermost) ql_nope.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mla_attention_03_amd import binding, synth
+from tests.helpers import bits16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _gpu(case):
+    return synth.RopeCase(case.ql_nope.to(DEV), case.q_pe.to(DEV), case.kv_c.to(DEV), case.k_pe.to(DEV),
+                          case.positions.to(DEV), case.cos_sin.to(DEV), case.slot_mapping.to(DEV),
+                          case.num_blocks, case.block_size)
+
+
+def _cache(case, kv_fp8):
+    # a recognisable fill, so rows that must stay untouched are checked too
+    N = case.num_blocks * case.block_size
+    fill = np.full((N, 576), 0x3C, dtype=np.uint8) if kv_fp8 else np.full((N, 576), 0x3F80, dtype=np.uint16)
+    return fill.reshape(case.num_blocks, case.block_size, 576)
+
+
+def _check(case, is_neox, q_fp8, kv_fp8, q_scale, kv_scale, ql_gpu=None):
+    g = _gpu(case)
+    fill = _cache(case, kv_fp8)
+    if kv_fp8:
+        cache = torch.from_numpy(fill.copy()).to(DEV)
+    else:
+        cache = torch.from_numpy(fill.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+    q_out = binding.sparse_mla_rope_concat_cache(
+        g.ql_nope if ql_gpu is None else ql_gpu, g.q_pe, g.kv_c, g.k_pe, g.positions, g.cos_sin,
+        is_neox, g.slot_mapping, cache, q_fp8=q_fp8, q_scale=q_scale, kv_scale=kv_scale)
+    torch.cuda.synchronize()
+    want_q, want_c = oracle.rope_concat_cache(
+        bits16(case.ql_nope), bits16(case.q_pe), bits16(case.kv_c), bits16(case.k_pe),
+        case.positions.numpy(), case.cos_sin.numpy(), is_neox, case.slot_mapping.numpy(), fill,
+        q_fp8=q_fp8, q_scale=q_scale, kv_scale=kv_scale)
+    got_q = q_out.cpu().view(torch.uint8 if q_fp8 else torch.int16).numpy().view(want_q.dtype)
+    got_c = cache.cpu().view(torch.uint8 if kv_fp8 else torch.int16).numpy().view(want_c.dtype)
+    assert np.array_equal(got_q, want_q), int((got_q != want_q).sum())
+    assert np.array_equal(got_c, want_c), int((got_c != want_c).sum())
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+@pytest.mark.parametrize("H", [16, 128])
+@pytest.mark.parametrize("bs", [1, 64])
+@pytest.mark.parametrize("q_fp8,kv_fp8", [(False, False), (True, True), (False, True)])
+def test_fused_rope_cache_bitwise(is_neox, H, bs, q_fp8, kv_fp8):
+    nb = 512 // bs
+    case = synth.make_rope_case(T=37, H=H, num_blocks=nb, block_size=bs, max_pos=4096,
+                                seed=H + bs + int(is_neox), skip_frac=0.15)
+    _check(case, is_neox, q_fp8, kv_fp8, q_scale=0.37, kv_scale=0.59)
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+def test_fused_rope_cache_strided_ql_nope(is_neox):
+    # the production layout: ql_nope is the output of a per-head bmm, stored
+    # heads-outermost and seen as [T, H, 512] through a transpose
+    case = synth.make_rope_case(T=29, H=16, num_blocks=8, block_size=64, seed=9)
+    heads_major = case.ql_nope.transpose(0, 1).contiguous().to(DEV)     # [H, T, 512]
+    ql = heads_major.transpose(0, 1)                                    # strided view
+    assert not ql.is_contiguous()
+    _check(case, is_neox, True, True, q_scale=0.37, kv_scale=0.59, ql_gpu=ql)
+
+
+def test_fused_outputs_feed_the_forward_pass():
+    """The fused op's e4m3 q and cache, fed to sparse_mla_fwd as pre-quantised q
+    over that pool, against the oracle run on the oracle's own fused outputs."""
+    T, H, nb, bs = 8, 16, 64, 64
+    case = synth.make_rope_case(T=T, H=H, num_blocks=nb, block_size=bs, max_pos=4096, seed=21)
+    # every slot written once: the first T slots come from the op, the rest from a second batch
+    N = nb * bs
+    extra = synth.make_rope_case(T=N, H=1, num_blocks=nb, block_size=bs, max_pos=4096, seed=22)
+    g, ge = _gpu(case), _gpu(extra)
+    q_scale, kv_scale = 0.02, 0.011
+    cache = torch.zeros((nb, bs, 576), dtype=torch.uint8, device=DEV)
+    binding.sparse_mla_rope_concat_cache(ge.ql_nope, ge.q_pe, ge.kv_c, ge.k_pe, ge.positions, ge.cos_sin,
+                                         True, ge.slot_mapping, cache, q_fp8=True, q_scale=q_scale,
+                                         kv_scale=kv_scale)
+    q8 = binding.sparse_mla_rope_concat_cache(g.ql_nope, g.q_pe, g.kv_c, g.k_pe, g.positions, g.cos_sin,
+                                              True, g.slot_mapping, cache, q_fp8=True, q_scale=q_scale,
+                                              kv_scale=kv_scale)
+    torch.cuda.synchronize()
+    # the oracle's own fused outputs, in the same order
+    c0 = np.zeros((nb, bs, 576), np.uint8)
+    _, c1 = oracle.rope_concat_cache(bits16(extra.ql_nope), bits16(extra.q_pe), bits16(extra.kv_c),
+                                     bits16(extra.k_pe), extra.positions.numpy(), extra.cos_sin.numpy(),
+                                     True, extra.slot_mapping.numpy(), c0, q_fp8=True, q_scale=q_scale,
+                                     kv_scale=kv_scale)
+    oq, c2 = oracle.rope_concat_cache(bits16(case.ql_nope), bits16(case.q_pe), bits16(case.kv_c),
+                                      bits16(case.k_pe), case.positions.numpy(), case.cos_sin.numpy(),
+                                      True, case.slot_mapping.numpy(), c1, q_fp8=True, q_scale=q_scale,
+                                      kv_scale=kv_scale)
+    assert np.array_equal(cache.cpu().numpy(), c2) and np.array_equal(q8.cpu().numpy(), oq)
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(N, 600, replace=False) for _ in range(T)]).astype(np.int32)
+    out, lse = binding.sparse_mla_fwd_ex(q8, cache, torch.from_numpy(idx).to(DEV), 1.0 / 24.0, kv_scale,
+                                         q_scale=q_scale)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.sparse_mla_fwd(oq, c2.reshape(N, 576), idx, 1.0 / 24.0, kv_scale,
+                                             q_mode=oracle.Q_GIVEN_FP8, q_scale=q_scale)
+    assert np.max(np.abs(out.float().cpu().numpy() - ref_out)) <= 6e-2
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= 1e-3

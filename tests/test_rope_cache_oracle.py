@@ -1,0 +1,175 @@
+"""Pins for the oracle of the fused q-RoPE / q-concat / KV-concat / cache write.
+
+The rotation and the bf16 rounding are checked against exact rational
+arithmetic (fractions.Fraction) on small inputs, the pair layouts against each
+other through the permutation that maps one onto the other, the e4m3 outputs
+against torch's own fp32 division and float8_e4m3fn cast, and the write rules
+(skipped slots, clamped positions, strided input) directly.
+"""
+from __future__ import annotations
+
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mla_attention_03_amd import synth
+from tests.helpers import bits16
+
+
+def _bf16_exact(bits: int) -> Fraction:
+    return Fraction(struct.unpack("<f", struct.pack("<I", (bits & 0xFFFF) << 16))[0])
+
+
+def _nearest_bf16(v: Fraction, approx: float) -> int:
+    """Brute force: the bf16 pattern nearest to the exact value v, ties to an even pattern."""
+    f32 = np.float32(approx)
+    b = int(np.frombuffer(f32.tobytes(), dtype=np.uint32)[0]) >> 16
+    best = None
+    for cand in {b - 1, b, b + 1, b + 2, b - 2}:
+        if cand < 0 or cand > 0xFFFF or (cand & 0x7F80) == 0x7F80:
+            continue
+        d = abs(_bf16_exact(cand) - v)
+        key = (d, cand & 1)
+        if best is None or key < best[0]:
+            best = (key, cand)
+    bits = best[1]
+    if v == 0:
+        return 0x8000 if str(approx).startswith("-") else 0
+    return bits
+
+
+def test_bf16_round_against_exact_search():
+    rng = np.random.default_rng(0)
+    vals = list(rng.standard_normal(2000) * np.exp(rng.uniform(-20, 20, 2000)))
+    # exact midpoints between neighbouring bf16 numbers, and just either side
+    for b in rng.integers(0x0080, 0x7F00, 300):
+        lo, hi = _bf16_exact(int(b)), _bf16_exact(int(b) + 1)
+        mid = (lo + hi) / 2
+        for v in (mid, mid + (hi - lo) / 1000, mid - (hi - lo) / 1000):
+            vals.append(float(v))
+            vals.append(-float(v))
+    for v in vals:
+        got = oracle.bf16_round(v)
+        want = _nearest_bf16(Fraction(v), v)
+        assert got == want, (v, hex(got), hex(want))
+
+
+def _case(T=3, H=2, seed=0, skip=0.0, nb=4, bs=64, max_pos=512):
+    return synth.make_rope_case(T, H, nb, bs, max_pos=max_pos, seed=seed, skip_frac=skip)
+
+
+def _run(case, is_neox, q_fp8=False, kv_fp8=False, q_scale=1.0, kv_scale=1.0, ql=None, cs=None, pos=None):
+    N = case.num_blocks * case.block_size
+    cache = np.zeros((N, 576), dtype=np.uint8 if kv_fp8 else np.uint16)
+    return oracle.rope_concat_cache(
+        bits16(case.ql_nope) if ql is None else ql, bits16(case.q_pe), bits16(case.kv_c),
+        bits16(case.k_pe), case.positions.numpy() if pos is None else pos,
+        case.cos_sin.numpy() if cs is None else cs, is_neox, case.slot_mapping.numpy(), cache,
+        q_fp8=q_fp8, q_scale=q_scale, kv_scale=kv_scale)
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+def test_rotation_exact(is_neox):
+    case = _case(T=2, H=2, seed=1)
+    q, cache = _run(case, is_neox)
+    qp = bits16(case.q_pe)
+    cs = case.cos_sin.numpy()
+    for t in range(2):
+        p = int(case.positions[t])
+        for h in range(2):
+            x = qp[t, h]
+            for i in range(32):
+                ix, iy = (i, i + 32) if is_neox else (2 * i, 2 * i + 1)
+                c, s = Fraction(float(cs[p, i])), Fraction(float(cs[p, 32 + i]))
+                a, b = _bf16_exact(int(x[ix])), _bf16_exact(int(x[iy]))
+                ex, ey = a * c - b * s, b * c + a * s
+                assert q[t, h, 512 + ix] == _nearest_bf16(ex, float(ex)), (t, h, i)
+                assert q[t, h, 512 + iy] == _nearest_bf16(ey, float(ey)), (t, h, i)
+        # the latent part and the cache row
+        assert np.array_equal(q[t, :, :512], bits16(case.ql_nope)[t])
+        slot = int(case.slot_mapping[t])
+        assert np.array_equal(cache[slot, :512], bits16(case.kv_c)[t])
+
+
+def test_zero_angle_is_the_plain_concat():
+    case = _case(T=4, H=3, seed=2)
+    cs = np.zeros((512, 64), np.float32)
+    cs[:, :32] = 1.0
+    for is_neox in (True, False):
+        q, cache = _run(case, is_neox, cs=cs)
+        assert np.array_equal(q[..., 512:], bits16(case.q_pe))
+        for t in range(4):
+            s = int(case.slot_mapping[t])
+            assert np.array_equal(cache[s], np.concatenate([bits16(case.kv_c)[t], bits16(case.k_pe)[t]]))
+
+
+def test_interleaved_is_rotate_halves_after_a_permutation():
+    # x' with x'[2i] = x[i], x'[2i+1] = x[i+32]: the interleaved RoPE of x' is
+    # the rotate-halves RoPE of x, moved by the same permutation
+    case = _case(T=3, H=4, seed=3)
+    perm = np.empty(64, np.int64)
+    perm[0::2] = np.arange(32)
+    perm[1::2] = np.arange(32) + 32
+    q_neox, c_neox = _run(case, True)
+    case_p = synth.RopeCase(case.ql_nope, case.q_pe[..., perm].contiguous(), case.kv_c,
+                            case.k_pe[:, perm].contiguous(), case.positions, case.cos_sin,
+                            case.slot_mapping, case.num_blocks, case.block_size)
+    q_gptj, c_gptj = _run(case_p, False)
+    assert np.array_equal(q_gptj[..., 512:], q_neox[..., 512:][..., perm])
+    assert np.array_equal(c_gptj[:, 512:], c_neox[:, 512:][:, perm])
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.37, 3.0])
+def test_e4m3_outputs_match_torch_division_and_cast(scale):
+    case = _case(T=3, H=2, seed=4)
+    qb, cb = _run(case, True)
+    q8, c8 = _run(case, True, q_fp8=True, kv_fp8=True, q_scale=scale, kv_scale=scale * 1.5)
+    def enc(bits, sc):
+        v = torch.from_numpy(bits.astype(np.int32) << 16).view(torch.float32)
+        y = torch.clamp(v / torch.tensor(np.float32(sc)), -448.0, 448.0)
+        return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q8, enc(qb, scale))
+    used = case.slot_mapping.numpy()
+    assert np.array_equal(c8[used], enc(cb[used], scale * 1.5))
+
+
+def test_skipped_slots_and_clamped_positions():
+    case = _case(T=6, H=2, seed=5, skip=0.5)
+    N = case.num_blocks * case.block_size
+    slots = case.slot_mapping.numpy().copy()
+    slots[0] = N + 3                       # out of range: no write either
+    case = synth.RopeCase(case.ql_nope, case.q_pe, case.kv_c, case.k_pe, case.positions,
+                          case.cos_sin, torch.from_numpy(slots), case.num_blocks, case.block_size)
+    q, cache = _run(case, True)
+    written = {int(s) for s in slots if 0 <= s < N}
+    for r in range(N):
+        if r not in written:
+            assert not cache[r].any()
+    pos = case.positions.numpy().copy()
+    pos_lo, pos_hi = pos.copy(), pos.copy()
+    pos_lo[1], pos_hi[1] = -7, 0
+    a, _ = _run(case, True, pos=pos_lo)
+    b, _ = _run(case, True, pos=pos_hi)
+    assert np.array_equal(a, b)
+    pos_lo[1], pos_hi[1] = 512 + 9, 511
+    a, _ = _run(case, True, pos=pos_lo)
+    b, _ = _run(case, True, pos=pos_hi)
+    assert np.array_equal(a, b)
+
+
+def test_strided_ql_nope_equals_contiguous():
+    case = _case(T=4, H=3, seed=6)
+    base = bits16(case.ql_nope)
+    wide = np.zeros((4, 3, 640), np.uint16)
+    wide[..., :512] = base
+    strided = wide[..., :512]              # row stride 640, not packed
+    trans = np.ascontiguousarray(base.transpose(1, 0, 2)).transpose(1, 0, 2)   # heads outermost
+    a, ca = _run(case, False)
+    b, cb = _run(case, False, ql=strided)
+    c, cc = _run(case, False, ql=trans)
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+    assert np.array_equal(ca, cb) and np.array_equal(ca, cc)
