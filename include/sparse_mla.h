@@ -149,6 +149,42 @@ smla_status_t sparse_mla_fwd_ex(const void* q, int64_t T, int64_t H, int64_t Dqk
                                 void* stream, const smla_options_t* opts);
 
 /*
+ * sparse_mla_fwd_varlen -- the forward pass for a batch whose tokens use lists
+ * of different lengths, e.g. decode tokens with full top-k lists next to early
+ * prefill rows with short ones (vLLM PR "[ROCm][DSv4.1][Perf] Route gfx942
+ * sparse MLA prefill to AITER pa_prefill_sparse", Gating and the review thread
+ * after Test plan: a path without a split of the list costs decode-sized calls
+ * about nine times more, so rows are routed by size).  Token t uses entries
+ * topk_idx[t, 0 .. topk_len[t]) of its row; the rest of the row is never read.
+ * The split over each list is chosen per token on the device: a token gets
+ * ceil(len / R) units of R entries (R from the batch shape and the CU count,
+ * a multiple of 64), and a token with one unit writes out / lse directly; the
+ * others are merged by the combine kernel.  A small planning kernel runs
+ * first (so the call stays capturable in a HIP graph: nothing comes back to
+ * the host).
+ *
+ *   topk_len   int32 [T] on the device; values are clamped into [0, K].
+ *   workspace  at least sparse_mla_workspace_bytes_varlen(T, H, K, Dqk, kv_dtype)
+ *              bytes, 16-byte aligned.
+ * Everything else as sparse_mla_fwd_ex; options.num_splits must be 0.
+ */
+smla_status_t sparse_mla_fwd_varlen(const void* q, int64_t T, int64_t H, int64_t Dqk,
+                                    int64_t q_stride_t, int64_t q_stride_h,
+                                    const void* kv_pool, int32_t kv_dtype,
+                                    int64_t num_blocks, int64_t block_size,
+                                    const int32_t* topk_idx, int64_t K, int64_t idx_stride_t,
+                                    const int32_t* topk_len,
+                                    float sm_scale, float kv_scale,
+                                    void* out, float* lse,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream, const smla_options_t* opts);
+
+/* Workspace bytes sparse_mla_fwd_varlen needs (queries the current device's
+ * CU count).  Returns (size_t)-1 on error. */
+size_t sparse_mla_workspace_bytes_varlen(int64_t T, int64_t H, int64_t K, int64_t Dqk,
+                                         int32_t kv_dtype);
+
+/*
  * Split-K factor a call with these sizes runs with.  num_splits = 0: the
  * library's choice for the current device (it queries the compute-unit count).
  * num_splits > 0: that request, validated (<= SMLA_MAX_SPLITS) and reduced to

@@ -72,9 +72,15 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sparse_mla_status_string.restype = ctypes.c_char_p
     lib.sparse_mla_last_error.argtypes = []
     lib.sparse_mla_last_error.restype = ctypes.c_char_p
-    lib.sparse_mla_rope_concat_cache.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, vp, i64, vp, vp, i64, i32,
-                                                  i64, i64, vp, i32, f32, vp, vp, i32, i64, i64, f32, vp]
-    lib.sparse_mla_rope_concat_cache.restype = ctypes.c_int
+    if path is None or hasattr(lib, "sparse_mla_fwd_varlen"):   # (a library built here always has them)
+        lib.sparse_mla_fwd_varlen.argtypes = fwd_args[:13] + [vp] + fwd_args[13:] + [ctypes.POINTER(Options)]
+        lib.sparse_mla_fwd_varlen.restype = ctypes.c_int
+        lib.sparse_mla_workspace_bytes_varlen.argtypes = [i64, i64, i64, i64, i32]
+        lib.sparse_mla_workspace_bytes_varlen.restype = sz
+    if path is None or hasattr(lib, "sparse_mla_rope_concat_cache"):
+        lib.sparse_mla_rope_concat_cache.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, vp, i64, vp, vp, i64,
+                                                      i32, i64, i64, vp, i32, f32, vp, vp, i32, i64, i64, f32, vp]
+        lib.sparse_mla_rope_concat_cache.restype = ctypes.c_int
     lib.sparse_mla_abi_version.argtypes = []
     lib.sparse_mla_abi_version.restype = i32
     if path is None:
@@ -292,3 +298,69 @@ def sparse_mla_rope_concat_cache(ql_nope: torch.Tensor, q_pe: torch.Tensor, kv_c
         float(kv_scale), _stream_handle(ql_nope.device, stream))
     _check(st)
     return q_out
+
+
+def sparse_mla_workspace_bytes_varlen(T: int, H: int, K: int, Dqk: int, kv_dtype: int) -> int:
+    n = load_library().sparse_mla_workspace_bytes_varlen(T, H, K, Dqk, kv_dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise SparseMLAError(2, load_library().sparse_mla_last_error().decode())
+    return n
+
+
+def sparse_mla_fwd_varlen(q: torch.Tensor, kv_pool: torch.Tensor, topk_idx: torch.Tensor,
+                          topk_len: torch.Tensor, sm_scale: float, kv_scale: float = 1.0,
+                          out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None, stream=None, sinks=None,
+                          dot_precision: int = 0, q_scale: float = 0.0):
+    """Forward pass with per-token list lengths: token t uses topk_idx[t, :topk_len[t]]
+    (int32 [T] on the device); the split over each list is chosen per token."""
+    lib = load_library()
+    if q_scale > 0:
+        if q.dim() != 3 or q.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError("pre-quantised q must be uint8 / float8_e4m3fn [T, H, Dqk]")
+    elif q.dim() != 3 or q.dtype != torch.bfloat16:
+        raise TypeError("q must be bfloat16 [T, H, Dqk]")
+    T, H, D = q.shape
+    if T > 0 and q.stride(2) != 1:
+        raise ValueError("q's last dimension must be contiguous")
+    nb, bs, Dkv = _pool_shape(kv_pool)
+    if Dkv != D or not kv_pool.is_contiguous():
+        raise ValueError("kv_pool must be contiguous with rows as wide as q's")
+    kvd = _kv_dtype(kv_pool)
+    if topk_idx.dim() != 2 or topk_idx.dtype != torch.int32 or topk_idx.shape[0] != T:
+        raise TypeError("topk_idx must be int32 [T, K]")
+    K = topk_idx.shape[1]
+    if T > 0 and K > 1 and topk_idx.stride(1) != 1:
+        raise ValueError("topk_idx rows must be contiguous")
+    if topk_len.shape != (T,) or topk_len.dtype != torch.int32 or not topk_len.is_contiguous():
+        raise TypeError("topk_len must be a contiguous int32 [T] tensor")
+    for t_, name in ((kv_pool, "kv_pool"), (topk_idx, "topk_idx"), (topk_len, "topk_len")):
+        if t_.device != q.device:
+            raise ValueError(f"{name} is on {t_.device}, q on {q.device}")
+    if out is None:
+        out = torch.empty((T, H, DV), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    ws_ptr, ws_bytes = None, 0
+    if T > 0:
+        need = sparse_mla_workspace_bytes_varlen(T, H, K, D, kvd)
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr = workspace.data_ptr()
+        ws_bytes = workspace.numel() * workspace.element_size()
+    opts = Options()
+    opts.dot_precision = dot_precision
+    opts.q_scale = float(q_scale)
+    if sinks is not None:
+        if sinks.shape != (H,) or sinks.dtype != torch.float32 or not sinks.is_contiguous():
+            raise ValueError("sinks must be a contiguous float32 [H] tensor")
+        opts.sinks = sinks.data_ptr()
+    st = lib.sparse_mla_fwd_varlen(
+        q.data_ptr(), T, H, D, q.stride(0) if T else 0, q.stride(1) if T else 0,
+        kv_pool.data_ptr(), kvd, nb, bs,
+        topk_idx.data_ptr() if topk_idx.numel() else None, K, topk_idx.stride(0) if T else 0,
+        topk_len.data_ptr() if T else None,
+        float(sm_scale), float(kv_scale), out.data_ptr(), lse.data_ptr(),
+        ws_ptr, ws_bytes, _stream_handle(q.device, stream), ctypes.byref(opts))
+    _check(st)
+    return out, lse

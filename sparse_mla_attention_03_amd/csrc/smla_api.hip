@@ -107,11 +107,49 @@ smla_status_t make_plan(int64_t T, int64_t H, int64_t K, int32_t req, Plan* plan
   return SMLA_OK;
 }
 
+// Per-token lengths: units of R entries, R chosen so that full lists would fill
+// the device about once (at least 4 tiles); at most S = ceil(K / R) units per
+// token.  Workspace: the unit table, the unit count, per-token first / count,
+// then partials and lse for every possible unit.
+struct VarlenLayout {
+  size_t units, count, first, tcount, part_o, part_lse, total;
+};
+VarlenLayout varlen_layout(int64_t T, int64_t H, int64_t S) {
+  auto up16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
+  VarlenLayout L{};
+  const size_t U = (size_t)T * S;
+  L.units = 0;
+  L.count = up16(L.units + U * 16);
+  L.first = L.count + 16;
+  L.tcount = up16(L.first + (size_t)T * 4);
+  L.part_o = up16(L.tcount + (size_t)T * 4);
+  L.part_lse = L.part_o + U * H * smla::kDV * sizeof(float);
+  L.total = L.part_lse + U * H * sizeof(float);
+  return L;
+}
+
+smla_status_t make_plan_varlen(int64_t T, int64_t H, int64_t K, Plan* plan) {
+  int cus = 0;
+  smla_status_t st = device_cu_count(&cus);
+  if (st != SMLA_OK) return st;
+  const int64_t HG = H / smla::heads_per_workgroup(H);
+  const int64_t tiles = (K + smla::kBK - 1) / smla::kBK;
+  int64_t rt = (T * HG * tiles + cus - 1) / cus;
+  if (rt < 4) rt = 4;
+  if (tiles > 0 && rt > tiles) rt = tiles;
+  plan->rps = (int32_t)(rt * smla::kBK);
+  const int64_t S = K > 0 ? (K + plan->rps - 1) / plan->rps : 1;
+  plan->S = (int32_t)S;
+  plan->ws_bytes = varlen_layout(T, H, S).total;
+  return SMLA_OK;
+}
+
 smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t q_stride_t,
                        int64_t q_stride_h, const void* kv_pool, int32_t kv_dtype, int64_t num_blocks,
                        int64_t block_size, const int32_t* topk_idx, int64_t K, int64_t idx_stride_t,
                        float sm_scale, float kv_scale, void* out, float* lse, void* workspace,
-                       size_t workspace_bytes, void* stream, const smla_options_t* opts) {
+                       size_t workspace_bytes, void* stream, const smla_options_t* opts,
+                       const int32_t* topk_len = nullptr) {
   g_last_error.clear();
   smla_status_t st = check_sizes(T, H, K, Dqk, kv_dtype);
   if (st != SMLA_OK) return st;
@@ -159,9 +197,15 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
   if (!aligned(out, 16)) return fail(SMLA_ERR_ALIGN, "out must be 16-byte aligned");
   if (!aligned(lse, 4) || (topk_idx && !aligned(topk_idx, 4)))
     return fail(SMLA_ERR_ALIGN, "lse and topk_idx must be 4-byte aligned");
+  const bool varlen = topk_len != nullptr;
+  if (varlen && !aligned(topk_len, 4)) return fail(SMLA_ERR_ALIGN, "topk_len must be 4-byte aligned");
+  if (varlen && req != 0)
+    return fail(SMLA_ERR_INVALID_ARG, "num_splits must be 0 with per-token lengths (the split is per token)");
+  if (varlen && T > 0x7fffffffLL / 64)
+    return fail(SMLA_ERR_UNSUPPORTED, "T=%lld too large for the per-token plan", (long long)T);
 
   Plan plan;
-  st = make_plan(T, H, K, req, &plan);
+  st = varlen ? make_plan_varlen(T, H, K, &plan) : make_plan(T, H, K, req, &plan);
   if (st != SMLA_OK) return st;
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes)
@@ -189,7 +233,17 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
   p.lse = lse;
   p.sinks = opts ? opts->sinks : nullptr;
   p.q_scale = q_scale;
-  if (plan.S > 1) {
+  const bool combine = varlen || plan.S > 1;
+  if (varlen) {
+    const VarlenLayout L = varlen_layout(T, H, plan.S);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    p.units = reinterpret_cast<const int4*>(ws + L.units);
+    p.num_units = reinterpret_cast<const int32_t*>(ws + L.count);
+    p.tok_first = reinterpret_cast<const int32_t*>(ws + L.first);
+    p.tok_count = reinterpret_cast<const int32_t*>(ws + L.tcount);
+    p.part_o = reinterpret_cast<float*>(ws + L.part_o);
+    p.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
+  } else if (plan.S > 1) {
     p.part_o = static_cast<float*>(workspace);
     p.part_lse = p.part_o + (size_t)plan.S * T * H * smla::kDV;
   }
@@ -199,9 +253,15 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
             plan.S, plan.rps);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  if (varlen) {
+    e = smla::launch_plan(topk_len, (int32_t)T, (int32_t)K, plan.rps, const_cast<int4*>(p.units),
+                          const_cast<int32_t*>(p.num_units), const_cast<int32_t*>(p.tok_first),
+                          const_cast<int32_t*>(p.tok_count), s);
+    if (e != hipSuccess) return fail(SMLA_ERR_HIP, "plan kernel launch: %s", hipGetErrorString(e));
+  }
   e = smla::launch_fwd(p, kv_dtype == SMLA_KV_FP8_E4M3, bf16_dots, (int)Dqk, s, ev0, ev1);
   if (e != hipSuccess) return fail(SMLA_ERR_HIP, "forward kernel launch: %s", hipGetErrorString(e));
-  if (plan.S > 1) {
+  if (combine) {
     e = smla::launch_combine(p, s);
     if (e != hipSuccess) return fail(SMLA_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
   }
@@ -211,6 +271,31 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
 }  // namespace
 
 extern "C" {
+
+smla_status_t sparse_mla_fwd_varlen(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t q_stride_t,
+                                    int64_t q_stride_h, const void* kv_pool, int32_t kv_dtype,
+                                    int64_t num_blocks, int64_t block_size, const int32_t* topk_idx, int64_t K,
+                                    int64_t idx_stride_t, const int32_t* topk_len, float sm_scale,
+                                    float kv_scale, void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream, const smla_options_t* opts) {
+  if (T > 0 && !topk_len) {
+    g_last_error.clear();
+    return fail(SMLA_ERR_NULL, "topk_len is required");
+  }
+  static const int32_t kNone = 0;
+  return fwd_impl(q, T, H, Dqk, q_stride_t, q_stride_h, kv_pool, kv_dtype, num_blocks, block_size, topk_idx,
+                  K, idx_stride_t, sm_scale, kv_scale, out, lse, workspace, workspace_bytes, stream, opts,
+                  T > 0 ? topk_len : &kNone);
+}
+
+size_t sparse_mla_workspace_bytes_varlen(int64_t T, int64_t H, int64_t K, int64_t Dqk, int32_t kv_dtype) {
+  g_last_error.clear();
+  if (check_sizes(T, H, K, Dqk, kv_dtype) != SMLA_OK) return (size_t)-1;
+  if (T == 0) return 0;
+  Plan plan;
+  if (make_plan_varlen(T, H, K, &plan) != SMLA_OK) return (size_t)-1;
+  return plan.ws_bytes;
+}
 
 smla_status_t sparse_mla_fwd(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t q_stride_t,
                              int64_t q_stride_h, const void* kv_pool, int32_t kv_dtype,

@@ -42,14 +42,53 @@ namespace smla {
 // Split partials are fp32 chunks of 4 columns; chunk c (columns 4c .. 4c+3) of
 // the 16 heads of a group sit side by side, so the 16 lanes that hold one chunk
 // of 16 consecutive heads store 256 contiguous bytes.  Index in 16-byte units.
-__device__ __forceinline__ int64_t part_chunk(const FwdParams& p, int s, int t, int head, int c) {
-  return (((int64_t)s * p.T + t) * p.H + (head & ~15)) * (kDV / 4) + 16 * c + (head & 15);
+// Partial row pr holds one unit's partials (uniform plan: pr = s T + t).
+__device__ __forceinline__ int64_t part_chunk(const FwdParams& p, int64_t pr, int head, int c) {
+  return (pr * p.H + (head & ~15)) * (kDV / 4) + 16 * c + (head & 15);
 }
 
-// Sink logit of a head in log2 units; only the final normalisation of an
-// unsplit call takes it (with splits the combine does).  -inf = no sink.
-__device__ __forceinline__ float sink_log2(const FwdParams& p, int head) {
-  return (p.S == 1 && p.sinks != nullptr) ? p.sinks[head] * kLog2e : -INFINITY;
+// A workgroup's unit of work: token t, entries [kbeg, kend) of its list, the
+// partial row of its result, and whether it is the token's only unit (then it
+// writes out / lse itself).  Uniform plan: S splits of rps entries per token;
+// per-token plan: a table the planner wrote.  False past the last unit.
+// The kernels decode (t, kbeg, kend) at entry and (prow, direct) only in the
+// epilogue, so the second pair is not held through the main loop.
+struct Unit {
+  int t, kbeg, kend;
+};
+__device__ __forceinline__ bool unit_of(const FwdParams& p, int u, Unit& w) {
+  if (p.units == nullptr) {
+    if (u >= p.T * p.S) return false;
+    w.t = u / p.S;
+    const int s = u - w.t * p.S;
+    w.kbeg = s * p.rps;
+    w.kend = min(w.kbeg + p.rps, p.K);
+    return true;
+  }
+  // the table entries are workgroup-uniform: keep them in scalar registers
+  if (u >= __builtin_amdgcn_readfirstlane(*p.num_units)) return false;
+  const int4 e = p.units[u];
+  w.t = __builtin_amdgcn_readfirstlane(e.x);
+  w.kbeg = __builtin_amdgcn_readfirstlane(e.y);
+  w.kend = __builtin_amdgcn_readfirstlane(e.z);
+  return true;
+}
+struct UnitTail {
+  int prow;
+  bool direct;
+};
+__device__ __forceinline__ UnitTail unit_tail(const FwdParams& p, int u) {
+  if (p.units == nullptr) {
+    const int t = u / p.S;
+    return UnitTail{(u - t * p.S) * p.T + t, p.S == 1};
+  }
+  return UnitTail{u, __builtin_amdgcn_readfirstlane(__atomic_load_n(&p.units[u].w, __ATOMIC_RELAXED)) != 0};
+}
+
+// Sink logit of a head in log2 units; only a unit that writes out itself takes
+// it (with splits the combine does).  -inf = no sink.
+__device__ __forceinline__ float sink_log2(const FwdParams& p, int head, bool direct) {
+  return (direct && p.sinks != nullptr) ? p.sinks[head] * kLog2e : -INFINITY;
 }
 
 // Final normalisation of one (token, head): m = the running max and l = the
@@ -164,12 +203,12 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
   const int L = blockIdx.x;
   const int hg = (L >> 3) % HG;
   const int u = ((L >> 3) / HG) * 8 + (L & 7);
-  if (u >= p.T * p.S) return;
-  const int t = u / p.S;
-  const int s = u - t * p.S;
+  Unit wu;
+  if (!unit_of(p, u, wu)) return;
+  const int t = wu.t;
   const int h0 = hg * HT;
-  const int kbeg = s * p.rps;
-  const int kend = min(kbeg + p.rps, p.K);
+  const int kbeg = wu.kbeg;
+  const int kend = wu.kend;
   const int ntiles = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
 
   const int head = h0 + ht * 16 + m16;
@@ -463,14 +502,15 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
   }
 
   // ---- epilogue ---------------------------------------------------------------
-  const float2 nz = finish_row(m_run, group4_sum(l_run), sink_log2(p, head), p.kv_scale);
+  const UnitTail wt = unit_tail(p, u);
+  const float2 nz = finish_row(m_run, group4_sum(l_run), sink_log2(p, head, wt.direct), p.kv_scale);
   const float scale = nz.x;
   const float lse_nat = nz.y;
   const int64_t th = (int64_t)t * p.H + head;
 #pragma unroll
   for (int a = 0; a < NSLOT; ++a) {
     const int d0 = dp * DPW + 128 * a + 32 * g;   // 32 contiguous columns of this lane
-    if (p.S == 1) {
+    if (wt.direct) {
       uint32_t w[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
@@ -481,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) dst[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
     } else {
-      f32x4* dst = reinterpret_cast<f32x4*>(p.part_o) + part_chunk(p, s, t, head, d0 / 4);
+      f32x4* dst = reinterpret_cast<f32x4*>(p.part_o) + part_chunk(p, wt.prow, head, d0 / 4);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         f32x4 v;
@@ -495,8 +535,8 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
     }
   }
   if (g == 0 && dp == 0) {
-    if (p.S == 1) p.lse[th] = lse_nat;
-    else p.part_lse[(int64_t)s * p.T * p.H + th] = lse_nat;
+    if (wt.direct) p.lse[th] = lse_nat;
+    else p.part_lse[(int64_t)wt.prow * p.H + head] = lse_nat;
   }
 }
 
@@ -552,12 +592,12 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   const int L = blockIdx.x;
   const int hg = (L >> 3) % HG;
   const int u = ((L >> 3) / HG) * 8 + (L & 7);
-  if (u >= p.T * p.S) return;
-  const int t = u / p.S;
-  const int s = u - t * p.S;
+  Unit wu;
+  if (!unit_of(p, u, wu)) return;
+  const int t = wu.t;
   const int h0 = hg * 16;
-  const int kbeg = s * p.rps;
-  const int kend = min(kbeg + p.rps, p.K);
+  const int kbeg = wu.kbeg;
+  const int kend = wu.kend;
   const int ntile = kend > kbeg ? (kend - kbeg + TR - 1) / TR : 0;
   const int nt = ntile > wave ? (ntile - wave + 3) / 4 : 0;   // this wave's tiles: wave + 4i
 
@@ -981,13 +1021,14 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
     f[w] = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][m16] - M);
     Lsum += f[w] * s_l[w][m16];
   }
-  const float2 nz = finish_row(M, Lsum, sink_log2(p, head), p.kv_scale);
+  const UnitTail wt = unit_tail(p, u);
+  const float2 nz = finish_row(M, Lsum, sink_log2(p, head, wt.direct), p.kv_scale);
   const float scale = nz.x;
-  if (p.S > 1) {
+  if (!wt.direct) {
     // 32 chunks x 16 heads of this wave's 128 columns, 8 per lane: store k
     // takes chunk 32 wave + 4k + g of head m16, so a store covers 1 KB of
     // consecutive partials
-    f32x4* dst = reinterpret_cast<f32x4*>(p.part_o) + part_chunk(p, s, t, head, 32 * wave + g);
+    f32x4* dst = reinterpret_cast<f32x4*>(p.part_o) + part_chunk(p, wt.prow, head, 32 * wave + g);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
@@ -1021,8 +1062,8 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   }
   if (wave == 0 && g == 0) {
     const int64_t th = (int64_t)t * p.H + head;
-    if (p.S == 1) p.lse[th] = nz.y;
-    else p.part_lse[(int64_t)s * p.T * p.H + th] = nz.y;
+    if (wt.direct) p.lse[th] = nz.y;
+    else p.part_lse[(int64_t)wt.prow * p.H + head] = nz.y;
   }
 }
 
@@ -1035,7 +1076,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
 // of PV, so each SIMD interleaves one score wave's and one output wave's MFMAs;
 // three LDS stages hold the tile being scored, the tile being multiplied and
 // the tile being filled, and one barrier per tile separates the phases.
-template <bool KV8, int DQK>
+template <bool KV8, int DQK, bool VL = false>
 __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
   using G = Geom<KV8, DQK>;
   constexpr int TR = KV8 ? 64 : 32;        // rows per tile (36 KiB for Dqk = 576 either way)
@@ -1073,12 +1114,24 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
   const int L = blockIdx.x;
   const int hg = (L >> 3) % HG;
   const int u = ((L >> 3) / HG) * 8 + (L & 7);
-  if (u >= p.T * p.S) return;
-  const int t = u / p.S;
-  const int s = u - t * p.S;
+  // VL: the per-token plan's table (a separate instantiation: the 64-head
+  // kernel has no registers to spare for a branch between the two)
+  int t, s, kbeg, kend;
+  if constexpr (!VL) {
+    if (u >= p.T * p.S) return;
+    t = u / p.S;
+    s = u - t * p.S;
+    kbeg = s * p.rps;
+    kend = min(kbeg + p.rps, p.K);
+  } else {
+    if (u >= __builtin_amdgcn_readfirstlane(*p.num_units)) return;
+    const int4 e = p.units[u];
+    t = __builtin_amdgcn_readfirstlane(e.x);
+    s = 0;
+    kbeg = __builtin_amdgcn_readfirstlane(e.y);
+    kend = __builtin_amdgcn_readfirstlane(e.z);
+  }
   const int h0 = hg * 64;
-  const int kbeg = s * p.rps;
-  const int kend = min(kbeg + p.rps, p.K);
   // tiles, rounded up to even: the score waves run two phases per trip with
   // no exit in between (an odd count gets one all-padding tile, which adds 0)
   const int nt = kend > kbeg ? (((kend - kbeg + TR - 1) / TR + 1) & ~1) : 0;
@@ -1429,13 +1482,14 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     }
 
     // ---- the output waves need the denominators; this wave writes lse
-    const float2 nz = finish_row(m_run, group4_sum(l_run), sink_log2(p, head), p.kv_scale);
+    const UnitTail wt = VL ? unit_tail(p, u) : UnitTail{s * p.T + t, p.S == 1};
+    const float2 nz = finish_row(m_run, group4_sum(l_run), sink_log2(p, head, wt.direct), p.kv_scale);
     if (g == 0) s_lfin[16 * qw + m16] = nz.x;
     __syncthreads();   // pairs with the output waves' last PV phase
     if (g == 0) {
       const int64_t th = (int64_t)t * p.H + head;
-      if (p.S == 1) p.lse[th] = nz.y;
-      else p.part_lse[(int64_t)s * p.T * p.H + th] = nz.y;
+      if (wt.direct) p.lse[th] = nz.y;
+      else p.part_lse[(int64_t)wt.prow * p.H + head] = nz.y;
     }
   } else {
     // =============================== output waves ==============================
@@ -1543,12 +1597,13 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
 
     // ---- epilogue: lane (m16, g) holds columns 128pw + 32g + 8i + e of head
     // 16hb + m16 in O[e][hb][i]
+    const UnitTail wt = VL ? unit_tail(p, u) : UnitTail{s * p.T + t, p.S == 1};
     const int d0 = 128 * pw + 32 * g;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
       const float scale = s_lfin[16 * hb + m16];
       const int64_t th = (int64_t)t * p.H + h0 + 16 * hb + m16;
-      if (p.S == 1) {
+      if (wt.direct) {
         u32x4* dst = reinterpret_cast<u32x4*>(p.out + th * kDV + d0);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -1561,7 +1616,7 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
           dst[k] = u32x4{w4[0], w4[1], w4[2], w4[3]};
         }
       } else {
-        f32x4* dst = reinterpret_cast<f32x4*>(p.part_o) + part_chunk(p, s, t, h0 + 16 * hb + m16, d0 / 4);
+        f32x4* dst = reinterpret_cast<f32x4*>(p.part_o) + part_chunk(p, wt.prow, h0 + 16 * hb + m16, d0 / 4);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           f32x4 v;
@@ -1592,22 +1647,30 @@ __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
   const int t = unit / HG, grp = unit - t * HG;
   const int hl = threadIdx.x & 15, cl = threadIdx.x >> 4;
   const int head = 16 * grp + hl;
-  const int64_t TH = (int64_t)p.T * p.H;
-  const float* pl = p.part_lse + (int64_t)t * p.H + head;
-  const f32x4* po = reinterpret_cast<const f32x4*>(p.part_o) + part_chunk(p, 0, t, head, 16 * slice + cl);
-  const int64_t sstride = TH * (kDV / 4);   // one split's partials, 16-byte units
+  // the token's partial rows: fr, fr + rs, ... (cnt of them)
+  int fr = t, rs = p.T, cnt = p.S;
+  if (p.tok_first != nullptr) {
+    fr = p.tok_first[t];
+    rs = 1;
+    cnt = p.tok_count[t];
+    if (cnt == 1) return;   // the token's only unit wrote out / lse itself
+  }
+  const float* pl = p.part_lse + (int64_t)fr * p.H + head;
+  const f32x4* po = reinterpret_cast<const f32x4*>(p.part_o) + part_chunk(p, fr, head, 16 * slice + cl);
+  const int64_t lstride = (int64_t)rs * p.H;                 // between partial rows, lse
+  const int64_t sstride = (int64_t)rs * p.H * (kDV / 4);     // ... and 16-byte chunks
   constexpr int B = 8;
   // a sink enters as one more split whose partial is zero: weight exp(sink - M)
   float M = p.sinks ? p.sinks[head] : -INFINITY;
   float W = (M == -INFINITY) ? 0.0f : 1.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < p.S; s0 += B) {
+  for (int s0 = 0; s0 < cnt; s0 += B) {
     float ls[B];
     f32x4 v[B];
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-      const int sj = min(s0 + j, p.S - 1);
-      ls[j] = (s0 + j < p.S) ? pl[sj * TH] : -INFINITY;
+      const int sj = min(s0 + j, cnt - 1);
+      ls[j] = (s0 + j < cnt) ? pl[sj * lstride] : -INFINITY;
       v[j] = po[sj * sstride];
     }
     float mb = M;
@@ -1667,6 +1730,53 @@ __global__ __launch_bounds__(kThreads) void smla_quantize_q_kernel(const uint16_
   if (threadIdx.x == 0) scales[(int64_t)t * G + gq] = s_q;
 }
 
+// ---- the per-token split plan: one workgroup scans the list lengths ---------------
+// count_t = max(1, ceil(len_t / R)) units of R entries (the last one shorter);
+// units are numbered token by token, and a token with one unit is direct.
+__global__ __launch_bounds__(1024) void smla_plan_kernel(const int32_t* lens, int32_t T, int32_t K, int32_t R,
+                                                         int4* units, int32_t* num_units, int32_t* tok_first,
+                                                         int32_t* tok_count) {
+  __shared__ int32_t s_part[32];
+  __shared__ int32_t s_carry;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < T; base += 1024) {
+    const int t = base + tid;
+    const int len = (t < T) ? min(max(lens[t], 0), K) : 0;
+    const int cnt = (t < T) ? max(1, (len + R - 1) / R) : 0;
+    // inclusive scan within the wave, then across the 16 waves
+    int x = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) s_part[wave] = x;
+    __syncthreads();
+    int before = s_carry;
+    for (int w = 0; w < wave; ++w) before += s_part[w];
+    const int first = before + x - cnt;
+    if (t < T) {
+      tok_first[t] = first;
+      tok_count[t] = cnt;
+      for (int j = 0; j < cnt; ++j)
+        units[first + j] = int4{t, j * R, min((j + 1) * R, len), cnt == 1 ? 1 : 0};
+    }
+    __syncthreads();
+    if (tid == 1023) s_carry = first + cnt;   // the last thread's end is the running total
+    __syncthreads();
+  }
+  if (tid == 0) *num_units = s_carry;
+}
+
+hipError_t launch_plan(const int32_t* lens, int32_t T, int32_t K, int32_t R, int4* units, int32_t* num_units,
+                       int32_t* tok_first, int32_t* tok_count, hipStream_t stream) {
+  hipLaunchKernelGGL(smla_plan_kernel, dim3(1), dim3(1024), 0, stream, lens, T, K, R, units, num_units,
+                     tok_first, tok_count);
+  return hipGetLastError();
+}
+
 // ---- launch wrappers ----------------------------------------------------------------
 template <bool KV8, int DQK, bool QB>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
@@ -1692,8 +1802,12 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream, hipEvent_
       hipExtLaunchKernelGGL((smla_tiles_kernel<KV8, DQK, 32, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
       break;
     default:
-      if constexpr (!QB)
-        hipExtLaunchKernelGGL((smla_heads_kernel<KV8, DQK>), gd, dim3(2 * kThreads), 0, stream, ev0, ev1, 0, p);
+      if constexpr (!QB) {
+        if (p.units != nullptr)
+          hipExtLaunchKernelGGL((smla_heads_kernel<KV8, DQK, true>), gd, dim3(2 * kThreads), 0, stream, ev0, ev1, 0, p);
+        else
+          hipExtLaunchKernelGGL((smla_heads_kernel<KV8, DQK, false>), gd, dim3(2 * kThreads), 0, stream, ev0, ev1, 0, p);
+      }
       break;
   }
   return hipGetLastError();

@@ -152,3 +152,24 @@ def test_quantize_entry_validation(lib):
     st = lib.sparse_mla_quantize_q_fp8(P, 2, 20, 512, 8192, 512, P, P, None)
     assert st == UNSUP
     assert lib.sparse_mla_quantize_q_fp8(None, 0, 16, 512, 0, 0, None, None, None) == OK
+
+
+def test_varlen_validation(lib):
+    opts = binding.Options()
+    lens = P
+    def v(**kw):
+        a = dict(q=P, T=4, H=16, D=512, qst=16 * 512, qsh=512, kv=P, dt=0, nb=16, bs=64, idx=P, K=128,
+                 ist=128, lens=lens, sm=0.04, kvs=1.0, out=P, lse=P, ws=P, wsb=1 << 30, splits=0)
+        a.update(kw)
+        opts.num_splits = a["splits"]
+        st = lib.sparse_mla_fwd_varlen(a["q"], a["T"], a["H"], a["D"], a["qst"], a["qsh"], a["kv"], a["dt"],
+                                       a["nb"], a["bs"], a["idx"], a["K"], a["ist"], a["lens"], a["sm"],
+                                       a["kvs"], a["out"], a["lse"], a["ws"], a["wsb"], None,
+                                       ctypes.byref(opts))
+        return st, binding.sparse_mla_last_error()
+    assert v(lens=None)[0] == NULL
+    st, msg = v(splits=2)
+    assert st == INVALID and "per token" in msg
+    st, msg = v(lens=P + 2)
+    assert st == ALIGN and "topk_len" in msg
+    assert v(T=0, q=None, kv=None, idx=None, out=None, lse=None, lens=None)[0] == OK
