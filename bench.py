@@ -281,6 +281,92 @@ def rope_cache_bench(args) -> None:
         "batch_ms": [round(b, 4) for b in batch_ms]}), flush=True)
 
 
+# Mixed batches: decode tokens with full top-2048 lists next to short lists
+# (64 .. 512 entries), one call; every token has its own paged context.
+# (heads, Dqk, context per token, decode tokens, short tokens)
+MIXED_WORKLOADS = {"mixed_bf16": (16, 512, 16384, 32, 480),
+                   "mixed_rope_bf16": (128, 576, 32768, 16, 112)}
+
+
+def _graph_us(fn, steps, warmup):
+    """Median of BATCHES graph replays of `steps` calls, in microseconds per call."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(BATCHES):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms.append(t0.elapsed_time(t1))
+    return float(np.median(ms)) / steps * 1e3, ms
+
+
+def mixed_bench(args) -> None:
+    """One JSON line: the per-token-length call on a mixed batch (gathered bytes of the
+    valid entries / time), with the same batch as one padded call beside it."""
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_03_amd import synth
+    from sparse_mla_attention_03_amd.binding import (sparse_mla_fwd_ex, sparse_mla_fwd_varlen,
+                                                     sparse_mla_workspace_bytes,
+                                                     sparse_mla_workspace_bytes_varlen)
+
+    H, D, ctx, Td, Ts = MIXED_WORKLOADS[args.workload]
+    T, K = Td + Ts, 2048
+    spec = synth.small_spec(T=T, H=H, Dqk=D, K=K, ctx=ctx, mode="decode", seed=8,
+                            sm_scale=1.0 / np.sqrt(D))
+    case = synth.make_case(spec, device="cuda:0")
+    rng = np.random.default_rng(8)
+    lens = np.concatenate([np.full(Td, K), rng.integers(64, 513, Ts)]).astype(np.int32)
+    idx = case.topk_idx.cpu().numpy().copy()
+    for t in range(T):
+        idx[t, lens[t]:] = -1
+    dev = torch.device("cuda:0")
+    idx_d, lens_d = torch.from_numpy(idx).to(dev), torch.from_numpy(lens).to(dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws_p = torch.empty(max(sparse_mla_workspace_bytes(T, H, K, D, 0, 0), 16), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(sparse_mla_workspace_bytes_varlen(T, H, K, D, 0), dtype=torch.uint8, device=dev)
+    us_v, batch_ms = _graph_us(lambda: sparse_mla_fwd_varlen(case.q, case.kv_pool, idx_d, lens_d, case.sm_scale,
+                                                              out=out, lse=lse, workspace=ws_v),
+                               args.steps, args.warmup)
+    us_p, _ = _graph_us(lambda: sparse_mla_fwd_ex(case.q, case.kv_pool, idx_d, case.sm_scale, out=out, lse=lse,
+                                                  workspace=ws_p), args.steps, args.warmup)
+    nbytes = int(lens.sum()) * D * 2
+    gbs = nbytes / (us_v * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "sparse-MLA mixed-batch gathered-KV HBM GB/s, per-token lengths (1 MI355X)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us_v / 1e3, 6), "us_per_call": round(us_v, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "heads": H, "dqk": D, "decode_tokens": Td, "short_tokens": Ts,
+                   "topk": K, "valid_entries": int(lens.sum()), "gathered_bytes_per_call": nbytes,
+                   "padded_call_us": round(us_p, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "batch_ms": [round(b, 4) for b in batch_ms]}), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic_summary:
@@ -297,6 +383,9 @@ def main():
         return
     if args.workload in ROPE_CACHE_WORKLOADS:
         rope_cache_bench(args)
+        return
+    if args.workload in MIXED_WORKLOADS:
+        mixed_bench(args)
         return
 
     import numpy as np

@@ -107,40 +107,34 @@ smla_status_t make_plan(int64_t T, int64_t H, int64_t K, int32_t req, Plan* plan
   return SMLA_OK;
 }
 
-// Per-token lengths: units of R entries, R chosen so that full lists would fill
-// the device about once (at least 4 tiles); at most S = ceil(K / R) units per
-// token.  Workspace: the unit table, the unit count, per-token first / count,
-// then partials and lse for every possible unit.
+// Per-token lengths: the planning kernel picks the unit length from the
+// batch's total; the host only sizes for it.  With HG head groups and C compute
+// units the batch has at most T + C / HG units and its split tokens fewer than
+// 2 C / HG partial rows (see smla_plan_kernel).  Workspace: the unit table, the
+// unit count, per-token first row / count, then partials and lse per row.
 struct VarlenLayout {
   size_t units, count, first, tcount, part_o, part_lse, total;
+  int32_t max_units, max_prows, HG, cus;
 };
-VarlenLayout varlen_layout(int64_t T, int64_t H, int64_t S) {
+smla_status_t varlen_layout(int64_t T, int64_t H, VarlenLayout* L) {
   auto up16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
-  VarlenLayout L{};
-  const size_t U = (size_t)T * S;
-  L.units = 0;
-  L.count = up16(L.units + U * 16);
-  L.first = L.count + 16;
-  L.tcount = up16(L.first + (size_t)T * 4);
-  L.part_o = up16(L.tcount + (size_t)T * 4);
-  L.part_lse = L.part_o + U * H * smla::kDV * sizeof(float);
-  L.total = L.part_lse + U * H * sizeof(float);
-  return L;
-}
-
-smla_status_t make_plan_varlen(int64_t T, int64_t H, int64_t K, Plan* plan) {
   int cus = 0;
   smla_status_t st = device_cu_count(&cus);
   if (st != SMLA_OK) return st;
   const int64_t HG = H / smla::heads_per_workgroup(H);
-  const int64_t tiles = (K + smla::kBK - 1) / smla::kBK;
-  int64_t rt = (T * HG * tiles + cus - 1) / cus;
-  if (rt < 4) rt = 4;
-  if (tiles > 0 && rt > tiles) rt = tiles;
-  plan->rps = (int32_t)(rt * smla::kBK);
-  const int64_t S = K > 0 ? (K + plan->rps - 1) / plan->rps : 1;
-  plan->S = (int32_t)S;
-  plan->ws_bytes = varlen_layout(T, H, S).total;
+  const int64_t per = (cus + HG - 1) / HG;
+  const int64_t U = T + per + 1, P = 2 * per + 1;
+  L->max_units = (int32_t)U;
+  L->max_prows = (int32_t)P;
+  L->HG = (int32_t)HG;
+  L->cus = cus;
+  L->units = 0;
+  L->count = up16((size_t)U * 16);
+  L->first = L->count + 16;
+  L->tcount = up16(L->first + (size_t)T * 4);
+  L->part_o = up16(L->tcount + (size_t)T * 4);
+  L->part_lse = L->part_o + (size_t)P * H * smla::kDV * sizeof(float);
+  L->total = L->part_lse + (size_t)P * H * sizeof(float);
   return SMLA_OK;
 }
 
@@ -198,6 +192,7 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
   if (!aligned(lse, 4) || (topk_idx && !aligned(topk_idx, 4)))
     return fail(SMLA_ERR_ALIGN, "lse and topk_idx must be 4-byte aligned");
   const bool varlen = topk_len != nullptr;
+  VarlenLayout VL{};
   if (varlen && !aligned(topk_len, 4)) return fail(SMLA_ERR_ALIGN, "topk_len must be 4-byte aligned");
   if (varlen && req != 0)
     return fail(SMLA_ERR_INVALID_ARG, "num_splits must be 0 with per-token lengths (the split is per token)");
@@ -205,7 +200,14 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
     return fail(SMLA_ERR_UNSUPPORTED, "T=%lld too large for the per-token plan", (long long)T);
 
   Plan plan;
-  st = varlen ? make_plan_varlen(T, H, K, &plan) : make_plan(T, H, K, req, &plan);
+  if (varlen) {
+    st = varlen_layout(T, H, &VL);
+    plan.S = 1;
+    plan.rps = 0;
+    plan.ws_bytes = VL.total;
+  } else {
+    st = make_plan(T, H, K, req, &plan);
+  }
   if (st != SMLA_OK) return st;
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes)
@@ -235,7 +237,7 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
   p.q_scale = q_scale;
   const bool combine = varlen || plan.S > 1;
   if (varlen) {
-    const VarlenLayout L = varlen_layout(T, H, plan.S);
+    const VarlenLayout& L = VL;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     p.units = reinterpret_cast<const int4*>(ws + L.units);
     p.num_units = reinterpret_cast<const int32_t*>(ws + L.count);
@@ -243,6 +245,8 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
     p.tok_count = reinterpret_cast<const int32_t*>(ws + L.tcount);
     p.part_o = reinterpret_cast<float*>(ws + L.part_o);
     p.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
+    p.max_units = L.max_units;
+    p.max_prows = L.max_prows;
   } else if (plan.S > 1) {
     p.part_o = static_cast<float*>(workspace);
     p.part_lse = p.part_o + (size_t)plan.S * T * H * smla::kDV;
@@ -254,9 +258,19 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (varlen) {
-    e = smla::launch_plan(topk_len, (int32_t)T, (int32_t)K, plan.rps, const_cast<int4*>(p.units),
-                          const_cast<int32_t*>(p.num_units), const_cast<int32_t*>(p.tok_first),
-                          const_cast<int32_t*>(p.tok_count), s);
+    smla::PlanParams q{};
+    q.lens = topk_len;
+    q.T = (int32_t)T;
+    q.K = (int32_t)K;
+    q.HG = VL.HG;
+    q.cus = VL.cus;
+    q.max_units = VL.max_units;
+    q.max_prows = VL.max_prows;
+    q.units = const_cast<int4*>(p.units);
+    q.num_units = const_cast<int32_t*>(p.num_units);
+    q.tok_first = const_cast<int32_t*>(p.tok_first);
+    q.tok_count = const_cast<int32_t*>(p.tok_count);
+    e = smla::launch_plan(q, s);
     if (e != hipSuccess) return fail(SMLA_ERR_HIP, "plan kernel launch: %s", hipGetErrorString(e));
   }
   e = smla::launch_fwd(p, kv_dtype == SMLA_KV_FP8_E4M3, bf16_dots, (int)Dqk, s, ev0, ev1);
@@ -292,9 +306,9 @@ size_t sparse_mla_workspace_bytes_varlen(int64_t T, int64_t H, int64_t K, int64_
   g_last_error.clear();
   if (check_sizes(T, H, K, Dqk, kv_dtype) != SMLA_OK) return (size_t)-1;
   if (T == 0) return 0;
-  Plan plan;
-  if (make_plan_varlen(T, H, K, &plan) != SMLA_OK) return (size_t)-1;
-  return plan.ws_bytes;
+  VarlenLayout L{};
+  if (varlen_layout(T, H, &L) != SMLA_OK) return (size_t)-1;
+  return L.total;
 }
 
 smla_status_t sparse_mla_fwd(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t q_stride_t,

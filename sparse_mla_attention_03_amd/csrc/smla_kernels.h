@@ -29,12 +29,14 @@ struct FwdParams {
   const float* sinks;           // fp32 [H] per-head sink logits (natural log), or null
   float q_scale;                // > 0: q holds e4m3 codes (byte strides), qhat = q_scale * code
   // per-token split plan (null = the uniform plan above): unit u covers
-  // entries [kbeg, kend) of token t, its partials are partial row u, and
-  // direct units (the token's only unit) write out / lse themselves
-  const int4* units;            // [U_max] {t, kbeg, kend, direct}
+  // entries [kbeg, kend) of token t; a split token's units write partial rows
+  // tok_first[t] .., a token's only unit (row -1) writes out / lse itself
+  const int4* units;            // [max_units] {t, kbeg, kend, partial row or -1 = direct}
   const int32_t* num_units;     // U (device)
-  const int32_t* tok_first;     // [T] first unit of each token
+  const int32_t* tok_first;     // [T] first partial row of each split token
   const int32_t* tok_count;     // [T] its unit count
+  int32_t max_units;            // upper bound on U (the grid is sized for it)
+  int32_t max_prows;            // partial rows in the workspace
 };
 
 // The fused q-RoPE / q-concat / KV-concat / cache write (strides in elements).
@@ -68,9 +70,17 @@ inline int heads_per_workgroup(int64_t H) { return (H % 64 == 0) ? 64 : (H % 32 
 hipError_t launch_fwd(const FwdParams& p, bool kv_fp8, bool bf16_dots, int dqk, hipStream_t stream,
                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_combine(const FwdParams& p, hipStream_t stream);
-// the per-token split plan from list lengths: count_t = max(1, ceil(len_t / R))
-hipError_t launch_plan(const int32_t* lens, int32_t T, int32_t K, int32_t R, int4* units, int32_t* num_units,
-                       int32_t* tok_first, int32_t* tok_count, hipStream_t stream);
+// the per-token split plan from list lengths (one workgroup)
+struct PlanParams {
+  const int32_t* lens;          // [T]
+  int32_t T, K, HG, cus;
+  int32_t max_units, max_prows;
+  int4* units;                  // [max_units] {t, kbeg, kend, partial row or -1}
+  int32_t* num_units;
+  int32_t* tok_first;           // [T] first partial row of a split token
+  int32_t* tok_count;           // [T] units of the token
+};
+hipError_t launch_plan(const PlanParams& q, hipStream_t stream);
 hipError_t launch_rope_cache(const RopeCacheParams& p, bool neox, bool q8, bool kv8, hipStream_t stream);
 hipError_t launch_quantize_q(const uint16_t* q, int64_t q_st, int64_t q_sh, int32_t T, int32_t H,
                              int dqk, uint8_t* codes, float* scales, hipStream_t stream);

@@ -82,7 +82,8 @@ __device__ __forceinline__ UnitTail unit_tail(const FwdParams& p, int u) {
     const int t = u / p.S;
     return UnitTail{(u - t * p.S) * p.T + t, p.S == 1};
   }
-  return UnitTail{u, __builtin_amdgcn_readfirstlane(__atomic_load_n(&p.units[u].w, __ATOMIC_RELAXED)) != 0};
+  const int pr = __builtin_amdgcn_readfirstlane(__atomic_load_n(&p.units[u].w, __ATOMIC_RELAXED));
+  return UnitTail{pr, pr < 0};   // a token's only unit has no partial row
 }
 
 // Sink logit of a head in log2 units; only a unit that writes out itself takes
@@ -1654,6 +1655,7 @@ __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
     rs = 1;
     cnt = p.tok_count[t];
     if (cnt == 1) return;   // the token's only unit wrote out / lse itself
+    cnt = max(0, min(cnt, p.max_prows - fr));
   }
   const float* pl = p.part_lse + (int64_t)fr * p.H + head;
   const f32x4* po = reinterpret_cast<const f32x4*>(p.part_o) + part_chunk(p, fr, head, 16 * slice + cl);
@@ -1731,49 +1733,76 @@ __global__ __launch_bounds__(kThreads) void smla_quantize_q_kernel(const uint16_
 }
 
 // ---- the per-token split plan: one workgroup scans the list lengths ---------------
-// count_t = max(1, ceil(len_t / R)) units of R entries (the last one shorter);
-// units are numbered token by token, and a token with one unit is direct.
-__global__ __launch_bounds__(1024) void smla_plan_kernel(const int32_t* lens, int32_t T, int32_t K, int32_t R,
-                                                         int4* units, int32_t* num_units, int32_t* tok_first,
-                                                         int32_t* tok_count) {
-  __shared__ int32_t s_part[32];
-  __shared__ int32_t s_carry;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) s_carry = 0;
-  __syncthreads();
-  for (int base = 0; base < T; base += 1024) {
-    const int t = base + tid;
-    const int len = (t < T) ? min(max(lens[t], 0), K) : 0;
-    const int cnt = (t < T) ? max(1, (len + R - 1) / R) : 0;
-    // inclusive scan within the wave, then across the 16 waves
-    int x = cnt;
+// With W = the batch's tiles (64 entries each, summed over tokens), units are
+// R = 64 max(4, ceil(W HG / CUs)) entries long, so the batch's units about fill
+// the device once; token t gets count_t = max(1, ceil(len_t / R)) of them.
+// Units are numbered token by token; the units of split tokens (count > 1) get
+// consecutive partial rows, a token's only unit gets -1 (it writes out / lse
+// itself).  Bounds (checked by the writes): units <= T + CUs / HG, partial
+// rows < 2 CUs / HG.
+__device__ __forceinline__ int block_sum_1024(int v, int* s_part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
-    if (lane == 63) s_part[wave] = x;
-    __syncthreads();
-    int before = s_carry;
-    for (int w = 0; w < wave; ++w) before += s_part[w];
-    const int first = before + x - cnt;
-    if (t < T) {
-      tok_first[t] = first;
-      tok_count[t] = cnt;
-      for (int j = 0; j < cnt; ++j)
-        units[first + j] = int4{t, j * R, min((j + 1) * R, len), cnt == 1 ? 1 : 0};
-    }
-    __syncthreads();
-    if (tid == 1023) s_carry = first + cnt;   // the last thread's end is the running total
-    __syncthreads();
-  }
-  if (tid == 0) *num_units = s_carry;
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if (lane == 0) s_part[wave] = v;
+  __syncthreads();
+  int t = 0;
+  for (int w = 0; w < 16; ++w) t += s_part[w];
+  return t;
 }
 
-hipError_t launch_plan(const int32_t* lens, int32_t T, int32_t K, int32_t R, int4* units, int32_t* num_units,
-                       int32_t* tok_first, int32_t* tok_count, hipStream_t stream) {
-  hipLaunchKernelGGL(smla_plan_kernel, dim3(1), dim3(1024), 0, stream, lens, T, K, R, units, num_units,
-                     tok_first, tok_count);
+__global__ __launch_bounds__(1024) void smla_plan_kernel(PlanParams q) {
+  __shared__ int32_t s_part[16], s_part2[16];
+  __shared__ int32_t s_carry[2];
+  __shared__ int32_t s_cut;   // first unit past a bound (none expected): no unit from it on runs
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // pass 1: the batch's tiles
+  int tiles = 0;
+  for (int t = tid; t < q.T; t += 1024) tiles += (min(max(q.lens[t], 0), q.K) + 63) / 64;
+  const int W = block_sum_1024(tiles, s_part);
+  const int rt = max(4, (int)(((int64_t)W * q.HG + q.cus - 1) / q.cus));
+  const int R = 64 * rt;
+  if (tid == 0) { s_carry[0] = 0; s_carry[1] = 0; s_cut = 0x7fffffff; }
+  __syncthreads();
+  // pass 2: units and partial rows, two scans at once
+  for (int base = 0; base < q.T; base += 1024) {
+    const int t = base + tid;
+    const int len = (t < q.T) ? min(max(q.lens[t], 0), q.K) : 0;
+    const int cnt = (t < q.T) ? max(1, (len + R - 1) / R) : 0;
+    const int sp = cnt > 1 ? cnt : 0;
+    int x = cnt, y = sp;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int xo = __shfl_up(x, o), yo = __shfl_up(y, o);
+      if (lane >= o) { x += xo; y += yo; }
+    }
+    if (lane == 63) { s_part[wave] = x; s_part2[wave] = y; }
+    __syncthreads();
+    int bu = s_carry[0], bp = s_carry[1];
+    for (int w = 0; w < wave; ++w) { bu += s_part[w]; bp += s_part2[w]; }
+    const int fu = bu + x - cnt, fp = bp + y - sp;
+    if (t < q.T) {
+      q.tok_first[t] = fp;
+      q.tok_count[t] = cnt;
+      for (int j = 0; j < cnt; ++j) {
+        const int pr = (cnt > 1) ? fp + j : -1;
+        if (fu + j < q.max_units && pr < q.max_prows)
+          q.units[fu + j] = int4{t, j * R, min((j + 1) * R, len), pr};
+        else
+          atomicMin(&s_cut, fu + j);
+      }
+    }
+    __syncthreads();
+    if (tid == 1023) { s_carry[0] = fu + cnt; s_carry[1] = fp + sp; }
+    __syncthreads();
+  }
+  __syncthreads();
+  if (tid == 0) *q.num_units = min(min(s_carry[0], q.max_units), s_cut);
+}
+
+hipError_t launch_plan(const PlanParams& q, hipStream_t stream) {
+  hipLaunchKernelGGL(smla_plan_kernel, dim3(1), dim3(1024), 0, stream, q);
   return hipGetLastError();
 }
 
@@ -1784,7 +1813,7 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream, hipEvent_
   // two 32-head groups)
   const int HT = QB ? (p.H % 32 == 0 ? 32 : 16) : heads_per_workgroup(p.H);
   const int HG = p.H / HT;
-  const int64_t units = (int64_t)p.T * p.S;
+  const int64_t units = p.units ? (int64_t)p.max_units : (int64_t)p.T * p.S;
   const int64_t grid = ((units + 7) / 8) * 8 * HG;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 gd((unsigned)grid), bd(kThreads);
