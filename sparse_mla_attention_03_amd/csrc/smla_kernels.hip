@@ -1640,6 +1640,7 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
 // splits are issued together (an empty split's partial is loaded but its
 // weight selects zero), so S <= 8 costs one memory round trip.  The bf16
 // result goes through LDS so that 8 lanes store one head's 128 bytes.
+template <bool VL>
 __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t s_out[16][64];
   const int HG = p.H / 16;
@@ -1650,10 +1651,11 @@ __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
   const int head = 16 * grp + hl;
   // the token's partial rows: fr, fr + rs, ... (cnt of them)
   int fr = t, rs = p.T, cnt = p.S;
-  if (p.tok_first != nullptr) {
-    fr = p.tok_first[t];
+  if constexpr (VL) {
+    // one token per workgroup: keep its values in scalar registers
+    fr = __builtin_amdgcn_readfirstlane(p.tok_first[t]);
     rs = 1;
-    cnt = p.tok_count[t];
+    cnt = __builtin_amdgcn_readfirstlane(p.tok_count[t]);
     if (cnt == 1) return;   // the token's only unit wrote out / lse itself
     cnt = max(0, min(cnt, p.max_prows - fr));
   }
@@ -1856,7 +1858,10 @@ hipError_t launch_fwd(const FwdParams& p, bool kv_fp8, bool bf16_dots, int dqk, 
 
 hipError_t launch_combine(const FwdParams& p, hipStream_t stream) {
   const dim3 gd((unsigned)((int64_t)p.T * (p.H / 16) * 8)), bd(kThreads);
-  hipLaunchKernelGGL(smla_combine_kernel, gd, bd, 0, stream, p);
+  if (p.tok_first != nullptr)
+    hipLaunchKernelGGL(smla_combine_kernel<true>, gd, bd, 0, stream, p);
+  else
+    hipLaunchKernelGGL(smla_combine_kernel<false>, gd, bd, 0, stream, p);
   return hipGetLastError();
 }
 
