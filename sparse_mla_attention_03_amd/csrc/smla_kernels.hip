@@ -1823,11 +1823,9 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream, hipEvent_
   // end timestamps (no marker packets around it)
   switch (HT) {
     case 16:
-      // 32-row wave tiles where four of them plus q fit in LDS, else 16
-      if constexpr (KV8 || DQK == 512)
-        hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 32, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
-      else
-        hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 16, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
+      // 16-row wave tiles: with 32 the tile in flight, the O accumulators and
+      // the product operands outgrow the register file and spill
+      hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 16, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
       break;
     case 32:
       hipExtLaunchKernelGGL((smla_tiles_kernel<KV8, DQK, 32, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
