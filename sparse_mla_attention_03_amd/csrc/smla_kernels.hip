@@ -1823,9 +1823,19 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream, hipEvent_
   // end timestamps (no marker packets around it)
   switch (HT) {
     case 16:
-      // 16-row wave tiles: with 32 the tile in flight, the O accumulators and
-      // the product operands outgrow the register file and spill
-      hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 16, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
+      // Split lists (decode: few rows per workgroup, bound by gather latency)
+      // take 16-row wave tiles -- more, shorter pipeline stages and a shorter
+      // tail after the last gather.  Whole lists (prefill, bound by LDS
+      // bandwidth) take 32-row tiles where four of them plus q fit in LDS: one
+      // q fragment read then feeds two 16-row blocks.
+      if constexpr (KV8 || DQK == 512) {
+        if (p.S > 1 || p.units != nullptr)
+          hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 16, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
+        else
+          hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 32, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
+      } else {
+        hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 16, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
+      }
       break;
     case 32:
       hipExtLaunchKernelGGL((smla_tiles_kernel<KV8, DQK, 32, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
