@@ -1634,18 +1634,24 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
 }
 
 // ---- split merge: out = sum_s w_s * O_s / sum_s w_s, w_s = exp(lse_s - max) ----
-// One workgroup per (token, 16-head group, 64 columns): thread (chunk tid >> 4,
-// head tid & 15) reads consecutive partials, so each split's 4 KB of the
-// workgroup arrive as whole lines.  The lse and partial loads of up to 8
-// splits are issued together (an empty split's partial is loaded but its
-// weight selects zero), so S <= 8 costs one memory round trip.  The bf16
-// result goes through LDS so that 8 lanes store one head's 128 bytes.
-template <bool VL>
+// One workgroup per (token, 16-head group, slice of 64 CPT columns): thread
+// (column cl = tid >> 4, head tid & 15) merges chunks cl + 16 k (k < CPT) of the
+// slice, so each split's partials of the workgroup arrive as whole lines.  The
+// lse and partial loads of B splits are issued together (B CPT of 8 - 16 bytes
+// in flight per lane; loads past the token's count are skipped and their
+// weight selects zero).  CPT grows with the batch (tokens x head groups) while
+// the grid keeps at least 512 workgroups: a short batch gets 8 narrow slices
+// per row, a long one fewer, longer-lived workgroups with more loads in
+// flight.  The bf16 result goes through LDS so that whole rows are stored.
+template <bool VL, int CPT>
 __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_out[16][64];
+  constexpr int NSL = 8 / CPT;                  // slices per (token, head group)
+  constexpr int B = CPT >= 4 ? 2 : 8 / CPT;     // splits per batch
+  constexpr int SROW = 64 * CPT + 8;            // padded LDS row (bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t s_out[16][SROW];
   const int HG = p.H / 16;
-  const int slice = blockIdx.x & 7;
-  const int unit = blockIdx.x >> 3;
+  const int slice = blockIdx.x % NSL;
+  const int unit = blockIdx.x / NSL;
   const int t = unit / HG, grp = unit - t * HG;
   const int hl = threadIdx.x & 15, cl = threadIdx.x >> 4;
   const int head = 16 * grp + hl;
@@ -1660,22 +1666,28 @@ __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
     cnt = max(0, min(cnt, p.max_prows - fr));
   }
   const float* pl = p.part_lse + (int64_t)fr * p.H + head;
-  const f32x4* po = reinterpret_cast<const f32x4*>(p.part_o) + part_chunk(p, fr, head, 16 * slice + cl);
+  const f32x4* po = reinterpret_cast<const f32x4*>(p.part_o) + part_chunk(p, fr, head, 16 * CPT * slice + cl);
   const int64_t lstride = (int64_t)rs * p.H;                 // between partial rows, lse
   const int64_t sstride = (int64_t)rs * p.H * (kDV / 4);     // ... and 16-byte chunks
-  constexpr int B = 8;
   // a sink enters as one more split whose partial is zero: weight exp(sink - M)
   float M = p.sinks ? p.sinks[head] : -INFINITY;
   float W = (M == -INFINITY) ? 0.0f : 1.0f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < cnt; s0 += B) {
     float ls[B];
-    f32x4 v[B];
+    f32x4 v[B][CPT];
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-      const int sj = min(s0 + j, cnt - 1);
-      ls[j] = (s0 + j < cnt) ? pl[sj * lstride] : -INFINITY;
-      v[j] = po[sj * sstride];
+      ls[j] = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) v[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s0 + j < cnt) {   // uniform
+        ls[j] = pl[(s0 + j) * lstride];
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) v[j][k] = po[(s0 + j) * sstride + 256 * k];   // chunk + 16 k
+      }
     }
     float mb = M;
 #pragma unroll
@@ -1684,25 +1696,30 @@ __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
     // rescale what was accumulated so far to the new running max
     const float r = __builtin_amdgcn_exp2f((M - mb) * kLog2e);
     W *= r;
-    acc *= r;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) acc[k] *= r;
     M = mb;
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const bool live = ls[j] != -INFINITY;
       const float w = live ? __builtin_amdgcn_exp2f((ls[j] - M) * kLog2e) : 0.0f;
       W += w;
-      acc += live ? w * v[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) acc[k] += live ? w * v[j][k] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   const float inv = (M == -INFINITY) ? 0.0f : 1.0f / W;   // all splits empty: +0
-  *reinterpret_cast<u32x2*>(&s_out[hl][4 * cl]) =
-      u32x2{pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
+#pragma unroll
+  for (int k = 0; k < CPT; ++k)
+    *reinterpret_cast<u32x2*>(&s_out[hl][4 * (cl + 16 * k)]) =
+        u32x2{pack_bf16(acc[k][0] * inv, acc[k][1] * inv), pack_bf16(acc[k][2] * inv, acc[k][3] * inv)};
   if (slice == 0 && cl == 0)
     p.lse[(int64_t)t * p.H + head] = (M == -INFINITY) ? -INFINITY : M + __builtin_amdgcn_logf(W) * kLn2;
   __syncthreads();
-  if (threadIdx.x < 128) {
-    const int h = threadIdx.x >> 3, k8 = threadIdx.x & 7;
-    *reinterpret_cast<u32x4*>(p.out + ((int64_t)t * p.H + 16 * grp + h) * kDV + 64 * slice + 8 * k8) =
+  // 16 rows of 128 CPT bytes, in 16-byte pieces
+  for (int i = threadIdx.x; i < 128 * CPT; i += kThreads) {
+    const int h = i / (8 * CPT), k8 = i - h * (8 * CPT);
+    *reinterpret_cast<u32x4*>(p.out + ((int64_t)t * p.H + 16 * grp + h) * kDV + 64 * CPT * slice + 8 * k8) =
         *reinterpret_cast<const u32x4*>(&s_out[h][8 * k8]);
   }
 }
@@ -1864,12 +1881,26 @@ hipError_t launch_fwd(const FwdParams& p, bool kv_fp8, bool bf16_dots, int dqk, 
                     : launch_fwd_t<false, 512, false>(p, stream, ev0, ev1);
 }
 
-hipError_t launch_combine(const FwdParams& p, hipStream_t stream) {
-  const dim3 gd((unsigned)((int64_t)p.T * (p.H / 16) * 8)), bd(kThreads);
+template <int CPT>
+static void launch_combine_t(const FwdParams& p, int64_t rows, hipStream_t stream) {
+  const dim3 gd((unsigned)(rows * (8 / CPT))), bd(kThreads);
   if (p.tok_first != nullptr)
-    hipLaunchKernelGGL(smla_combine_kernel<true>, gd, bd, 0, stream, p);
+    hipLaunchKernelGGL((smla_combine_kernel<true, CPT>), gd, bd, 0, stream, p);
   else
-    hipLaunchKernelGGL(smla_combine_kernel<false>, gd, bd, 0, stream, p);
+    hipLaunchKernelGGL((smla_combine_kernel<false, CPT>), gd, bd, 0, stream, p);
+}
+
+hipError_t launch_combine(const FwdParams& p, hipStream_t stream) {
+  // (token, head group) rows; the widest slices that leave >= 512 workgroups
+  const int64_t rows = (int64_t)p.T * (p.H / 16);
+  int cpt = 1;
+  while (cpt < 8 && rows * (8 / (2 * cpt)) >= 512) cpt *= 2;
+  switch (cpt) {
+    case 1: launch_combine_t<1>(p, rows, stream); break;
+    case 2: launch_combine_t<2>(p, rows, stream); break;
+    case 4: launch_combine_t<4>(p, rows, stream); break;
+    default: launch_combine_t<8>(p, rows, stream); break;
+  }
   return hipGetLastError();
 }
 

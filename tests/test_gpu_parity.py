@@ -210,6 +210,17 @@ def test_split_invariance_and_determinism(kv):
         assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(l, l2)
 
 
+# The split merge widens its slices with the number of (token, 16-head group)
+# rows: 80 rows -> 1 chunk per thread, 192 -> 2, 320 -> 4, 528 -> 8.
+@pytest.mark.parametrize("T,H,kv", [(10, 128, "bf16"), (24, 128, "fp8"), (40, 128, "bf16"), (33, 256, "fp8")])
+def test_merge_widths_parity(T, H, kv):
+    case = gpu_case(T=T, H=H, Dqk=576, K=200, ctx=4096, kv_dtype=kv, seed=T + H)
+    ref_out, ref_lse = oracle_for_tokens(case)
+    for s in (2, 5):
+        out, lse = run(case, num_splits=s)
+        compare(out, lse, ref_out, ref_lse, kv, f"merge T{T} H{H} {kv} S{s}")
+
+
 @pytest.mark.parametrize("H,D", [(16, 512), (64, 576), (128, 512)])
 @pytest.mark.parametrize("growing", [True, False])
 def test_scores_that_keep_growing(H, D, growing):

@@ -54,6 +54,8 @@ VARLEN_CASES = [
     (9, 32, 512, 300, 2048, "fp8"),      # 32-head kernel
     (9, 64, 576, 520, 2048, "bf16"),     # 64 heads, as two 32-head groups
     (8, 128, 512, 1100, 4096, "fp8"),
+    (24, 128, 576, 400, 4096, "bf16"),   # 192 (token, 16-head) rows: the merge's 2-chunk slices
+    (40, 128, 512, 300, 2048, "fp8"),    # 320 rows: 4-chunk slices
 ]
 
 
