@@ -36,6 +36,9 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // Compute units of the current device, cached per device id (read-only after
 // the first query; benign races write the same value).
 constexpr int kMaxDevices = 64;
+// workspace bytes per (split, token, head) partial row: 512 fp16 values, four
+// fp32 quarter scales and one fp32 lse
+constexpr size_t kPartRowBytes = smla::kDV * sizeof(uint16_t) + 4 * sizeof(float) + sizeof(float);
 std::atomic<int> g_cu_count[kMaxDevices];
 
 smla_status_t device_cu_count(int* cus) {
@@ -58,7 +61,7 @@ smla_status_t device_cu_count(int* cus) {
 struct Plan {
   int32_t S = 1;        // split-K factor
   int32_t rps = 0;      // top-k entries per split (multiple of kBK)
-  size_t ws_bytes = 0;  // workspace: S*T*H*512 fp32 partials + S*T*H fp32 lse
+  size_t ws_bytes = 0;  // workspace: S*T*H*512 fp16 partials, S*T*H*4 fp32 scales, S*T*H fp32 lse
 };
 
 smla_status_t check_sizes(int64_t T, int64_t H, int64_t K, int64_t Dqk, int32_t kv_dtype) {
@@ -103,7 +106,7 @@ smla_status_t make_plan(int64_t T, int64_t H, int64_t K, int32_t req, Plan* plan
   if (tiles > 0) S = (tiles + tps - 1) / tps;                 // drop empty splits
   plan->S = (int32_t)S;
   plan->rps = (int32_t)(tps * smla::kBK);
-  plan->ws_bytes = S > 1 ? (size_t)S * T * H * (smla::kDV + 1) * sizeof(float) : 0;
+  plan->ws_bytes = S > 1 ? (size_t)S * T * H * kPartRowBytes : 0;
   return SMLA_OK;
 }
 
@@ -113,7 +116,7 @@ smla_status_t make_plan(int64_t T, int64_t H, int64_t K, int32_t req, Plan* plan
 // 2 C / HG partial rows (see smla_plan_kernel).  Workspace: the unit table, the
 // unit count, per-token first row / count, then partials and lse per row.
 struct VarlenLayout {
-  size_t units, count, first, tcount, part_o, part_lse, total;
+  size_t units, count, first, tcount, part_o, part_scale, part_lse, total;
   int32_t max_units, max_prows, HG, cus;
 };
 smla_status_t varlen_layout(int64_t T, int64_t H, VarlenLayout* L) {
@@ -133,7 +136,8 @@ smla_status_t varlen_layout(int64_t T, int64_t H, VarlenLayout* L) {
   L->first = L->count + 16;
   L->tcount = up16(L->first + (size_t)T * 4);
   L->part_o = up16(L->tcount + (size_t)T * 4);
-  L->part_lse = L->part_o + (size_t)P * H * smla::kDV * sizeof(float);
+  L->part_scale = L->part_o + (size_t)P * H * smla::kDV * sizeof(uint16_t);
+  L->part_lse = L->part_scale + (size_t)P * H * 4 * sizeof(float);
   L->total = L->part_lse + (size_t)P * H * sizeof(float);
   return SMLA_OK;
 }
@@ -243,13 +247,16 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
     p.num_units = reinterpret_cast<const int32_t*>(ws + L.count);
     p.tok_first = reinterpret_cast<const int32_t*>(ws + L.first);
     p.tok_count = reinterpret_cast<const int32_t*>(ws + L.tcount);
-    p.part_o = reinterpret_cast<float*>(ws + L.part_o);
+    p.part_o = reinterpret_cast<uint16_t*>(ws + L.part_o);
+    p.part_scale = reinterpret_cast<float*>(ws + L.part_scale);
     p.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
     p.max_units = L.max_units;
     p.max_prows = L.max_prows;
   } else if (plan.S > 1) {
-    p.part_o = static_cast<float*>(workspace);
-    p.part_lse = p.part_o + (size_t)plan.S * T * H * smla::kDV;
+    const size_t rows = (size_t)plan.S * T * H;   // (split, token, head) partial rows
+    p.part_o = static_cast<uint16_t*>(workspace);
+    p.part_scale = reinterpret_cast<float*>(p.part_o + rows * smla::kDV);
+    p.part_lse = p.part_scale + rows * 4;
   }
   if (getenv("SPARSEMLA_LOG"))
     fprintf(stderr, "[sparsemla] T=%lld H=%lld Dqk=%lld K=%lld kv=%s splits=%d rows/split=%d\n",

@@ -23,9 +23,10 @@ struct FwdParams {
   float sm_scale, kv_scale;
   uint16_t* out;                // bf16 [T, H, 512]
   float* lse;                   // fp32 [T, H]
-  float* part_o;                // fp32 [S, T, H/16, 128, 16, 4] (S > 1): 16-byte column
-                                // chunk c of the 16 heads of a group side by side
-  float* part_lse;              // fp32 [S, T, H]      (S > 1)
+  uint16_t* part_o;             // fp16 [P, H/16, 128, 16, 4] (split calls): 4-column chunk c
+                                // of the 16 heads of a group side by side
+  float* part_scale;            // fp32 [P, H, 4]: power-of-two scale of each 128-column quarter
+  float* part_lse;              // fp32 [P, H]
   const float* sinks;           // fp32 [H] per-head sink logits (natural log), or null
   float q_scale;                // > 0: q holds e4m3 codes (byte strides), qhat = q_scale * code
   // per-token split plan (null = the uniform plan above): unit u covers

@@ -39,12 +39,44 @@
 
 namespace smla {
 
-// Split partials are fp32 chunks of 4 columns; chunk c (columns 4c .. 4c+3) of
-// the 16 heads of a group sit side by side, so the 16 lanes that hold one chunk
-// of 16 consecutive heads store 256 contiguous bytes.  Index in 16-byte units.
+// Split partials are chunks of 4 columns; chunk c (columns 4c .. 4c+3) of the
+// 16 heads of a group sit side by side, so the 16 lanes that hold one chunk of
+// 16 consecutive heads store contiguous bytes.  Index in chunks (8 bytes).
 // Partial row pr holds one unit's partials (uniform plan: pr = s T + t).
 __device__ __forceinline__ int64_t part_chunk(const FwdParams& p, int64_t pr, int head, int c) {
   return (pr * p.H + (head & ~15)) * (kDV / 4) + 16 * c + (head & 15);
+}
+
+// A chunk is stored as four fp16 numbers against a power-of-two scale 2^e per
+// (partial row, head, 128-column quarter), e the binary exponent of the
+// quarter's largest magnitude: every stored number lies in (-2, 2), so it keeps
+// 11 significant bits relative to that largest value, over fp32's whole
+// exponent range, in half the bytes of fp32.  Zero and subnormal maxima take
+// e = -126; inf / nan take e = 0 and are stored as they are.
+__device__ __forceinline__ int part_exp(float amax) {
+  const int eb = (int)((__float_as_uint(amax) >> 23) & 0xff);
+  return eb == 0xff ? 0 : max(eb, 1) - 127;
+}
+// the largest magnitude over the four lanes m16 + 16 g that hold one quarter
+__device__ __forceinline__ float quarter_max(float a) {
+  a = fmaxf(a, __shfl_xor(a, 16));
+  return fmaxf(a, __shfl_xor(a, 32));
+}
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;   // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+__device__ __forceinline__ u32x2 part_encode(const f32x4& v, int e) {
+  return u32x2{pack_f16(ldexpf(v[0], -e), ldexpf(v[1], -e)), pack_f16(ldexpf(v[2], -e), ldexpf(v[3], -e))};
+}
+__device__ __forceinline__ f32x4 part_decode(const u32x2& w) {
+  return f32x4{(float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] & 0xffffu)),
+               (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] >> 16)),
+               (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] & 0xffffu)),
+               (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] >> 16))};
+}
+__device__ __forceinline__ void part_store_scale(const FwdParams& p, int64_t pr, int head, int quarter, int e) {
+  p.part_scale[(pr * p.H + head) * 4 + quarter] = ldexpf(1.0f, e);
 }
 
 // A workgroup's unit of work: token t, entries [kbeg, kend) of its list, the
@@ -522,7 +554,11 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) dst[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
     } else {
-      f32x4* dst = reinterpret_cast<f32x4*>(p.part_o) + part_chunk(p, wt.prow, head, d0 / 4);
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(O[a][j & 7][j >> 3]));
+      const int e = part_exp(quarter_max(amax * scale));   // rounding is monotonic
+      u32x2* dst = reinterpret_cast<u32x2*>(p.part_o) + part_chunk(p, wt.prow, head, d0 / 4);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         f32x4 v;
@@ -531,8 +567,9 @@ __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
           const int j = 4 * k + x;
           v[x] = O[a][j & 7][j >> 3] * scale;
         }
-        dst[16 * k] = v;
+        dst[16 * k] = part_encode(v, e);
       }
+      if (g == 0) part_store_scale(p, wt.prow, head, (dp * DPW + 128 * a) / 128, e);
     }
   }
   if (g == 0 && dp == 0) {
@@ -1029,15 +1066,22 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
     // 32 chunks x 16 heads of this wave's 128 columns, 8 per lane: store k
     // takes chunk 32 wave + 4k + g of head m16, so a store covers 1 KB of
     // consecutive partials
-    f32x4* dst = reinterpret_cast<f32x4*>(p.part_o) + part_chunk(p, wt.prow, head, 32 * wave + g);
+    f32x4 vv[8];
+    float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < 4; ++w)
         v += f[w] * *reinterpret_cast<const f32x4*>(ob + (w * 16 + m16) * OPAD + 128 * wave + 4 * (4 * k + g));
-      dst[64 * k] = v * scale;
+      vv[k] = v * scale;
+      amax = fmaxf(fmaxf(amax, fmaxf(fabsf(vv[k][0]), fabsf(vv[k][1]))), fmaxf(fabsf(vv[k][2]), fabsf(vv[k][3])));
     }
+    const int e = part_exp(quarter_max(amax));   // this wave's columns are quarter `wave`
+    u32x2* dst = reinterpret_cast<u32x2*>(p.part_o) + part_chunk(p, wt.prow, head, 32 * wave + g);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dst[64 * k] = part_encode(vv[k], e);
+    if (g == 0) part_store_scale(p, wt.prow, head, wave, e);
   } else {
     // 16 heads x 16 chunks of 8 columns, 4 per lane: store k takes head 4k + g,
     // columns 128 wave + 8 m16 .. + 8, so 16 lanes write a head's 256 bytes;
@@ -1617,7 +1661,11 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
           dst[k] = u32x4{w4[0], w4[1], w4[2], w4[3]};
         }
       } else {
-        f32x4* dst = reinterpret_cast<f32x4*>(p.part_o) + part_chunk(p, wt.prow, h0 + 16 * hb + m16, d0 / 4);
+        float amax = 0.0f;
+#pragma unroll
+        for (int jx = 0; jx < 32; ++jx) amax = fmaxf(amax, fabsf(O[jx & 7][hb][jx >> 3]));
+        const int e = part_exp(quarter_max(amax * scale));   // rounding is monotonic
+        u32x2* dst = reinterpret_cast<u32x2*>(p.part_o) + part_chunk(p, wt.prow, h0 + 16 * hb + m16, d0 / 4);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           f32x4 v;
@@ -1626,8 +1674,9 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
             const int jx = 4 * k + x;
             v[x] = O[jx & 7][hb][jx >> 3] * scale;
           }
-          dst[16 * k] = v;
+          dst[16 * k] = part_encode(v, e);
         }
+        if (g == 0) part_store_scale(p, wt.prow, h0 + 16 * hb + m16, pw, e);
       }
     }
   }
@@ -1665,10 +1714,13 @@ __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
     if (cnt == 1) return;   // the token's only unit wrote out / lse itself
     cnt = max(0, min(cnt, p.max_prows - fr));
   }
+  constexpr int NQ = (CPT + 1) / 2;             // quarters the lane's chunks fall in
   const float* pl = p.part_lse + (int64_t)fr * p.H + head;
-  const f32x4* po = reinterpret_cast<const f32x4*>(p.part_o) + part_chunk(p, fr, head, 16 * CPT * slice + cl);
-  const int64_t lstride = (int64_t)rs * p.H;                 // between partial rows, lse
-  const int64_t sstride = (int64_t)rs * p.H * (kDV / 4);     // ... and 16-byte chunks
+  const float* pc = p.part_scale + ((int64_t)fr * p.H + head) * 4 + CPT * slice / 2;
+  const u32x2* po = reinterpret_cast<const u32x2*>(p.part_o) + part_chunk(p, fr, head, 16 * CPT * slice + cl);
+  const int64_t lstride = (int64_t)rs * p.H;                 // between partial rows: lse,
+  const int64_t cstride = 4 * lstride;                       // quarter scales
+  const int64_t sstride = (int64_t)rs * p.H * (kDV / 4);     // and chunks
   // a sink enters as one more split whose partial is zero: weight exp(sink - M)
   float M = p.sinks ? p.sinks[head] : -INFINITY;
   float W = (M == -INFINITY) ? 0.0f : 1.0f;
@@ -1676,15 +1728,19 @@ __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
 #pragma unroll
   for (int k = 0; k < CPT; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < cnt; s0 += B) {
-    float ls[B];
-    f32x4 v[B][CPT];
+    float ls[B], cs[B][NQ];
+    u32x2 v[B][CPT];
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       ls[j] = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) v[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < NQ; ++k) cs[j][k] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) v[j][k] = u32x2{0u, 0u};
       if (s0 + j < cnt) {   // uniform
         ls[j] = pl[(s0 + j) * lstride];
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) cs[j][k] = pc[(s0 + j) * cstride + k];
 #pragma unroll
         for (int k = 0; k < CPT; ++k) v[j][k] = po[(s0 + j) * sstride + 256 * k];   // chunk + 16 k
       }
@@ -1705,7 +1761,8 @@ __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
       const float w = live ? __builtin_amdgcn_exp2f((ls[j] - M) * kLog2e) : 0.0f;
       W += w;
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) acc[k] += live ? w * v[j][k] : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < CPT; ++k)   // chunk cl + 16 k lies in quarter CPT slice / 2 + k / 2
+        acc[k] += live ? (w * cs[j][k / 2]) * part_decode(v[j][k]) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   const float inv = (M == -INFINITY) ? 0.0f : 1.0f / W;   // all splits empty: +0

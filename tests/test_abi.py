@@ -135,7 +135,8 @@ def test_validation_errors(lib, kw, status, needle):
 def test_workspace_and_split_planning_explicit(lib):
     # explicit split counts need no device query
     assert binding.sparse_mla_workspace_bytes(32, 16, 2048, 512, 0, 1) == 0
-    assert binding.sparse_mla_workspace_bytes(32, 16, 2048, 512, 0, 8) == 8 * 32 * 16 * 513 * 4
+    # per (split, token, head): 512 fp16 partials, four fp32 quarter scales, one fp32 lse
+    assert binding.sparse_mla_workspace_bytes(32, 16, 2048, 512, 0, 8) == 8 * 32 * 16 * (1024 + 16 + 4)
     # never more splits than 64-entry tiles; empty splits are dropped
     assert binding.sparse_mla_num_splits(4, 16, 128, 512, 0, 8) == 2
     assert binding.sparse_mla_num_splits(4, 16, 200, 512, 0, 3) == 2   # 4 tiles -> 2+2
