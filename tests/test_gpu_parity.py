@@ -221,6 +221,26 @@ def test_merge_widths_parity(T, H, kv):
         compare(out, lse, ref_out, ref_lse, kv, f"merge T{T} H{H} {kv} S{s}")
 
 
+# Split partials are fp16 against a power-of-two scale per quarter row, so the
+# merge must pass outputs of any magnitude through.  V is scaled by 2^e (bf16:
+# the pool itself, fp8: kv_scale) and sm_scale by 2^-e: the logits are
+# bit-identical, the output is the oracle's times 2^e.
+@pytest.mark.parametrize("H,kv,e", [(16, "bf16", 90), (16, "bf16", -60), (128, "bf16", 100),
+                                    (16, "fp8", 80), (128, "fp8", -70)])
+def test_split_partials_keep_the_range(H, kv, e):
+    case = gpu_case(T=5, H=H, Dqk=576 if H == 128 else 512, K=700, ctx=4096, kv_dtype=kv, seed=H + abs(e))
+    f = 2.0 ** e
+    if kv == "bf16":
+        pool, kv_scale = (case.kv_pool.float() * f).to(torch.bfloat16), case.kv_scale
+    else:
+        pool, kv_scale = case.kv_pool, case.kv_scale * f
+    out, lse = sparse_mla_fwd_ex(case.q, pool, case.topk_idx, case.sm_scale / f, kv_scale, num_splits=4)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_for_tokens(case)
+    back = torch.from_numpy(out.float().cpu().numpy().astype(np.float64) / f)
+    compare(back, lse, ref_out, ref_lse, kv, f"range 2^{e} H{H} {kv}")
+
+
 @pytest.mark.parametrize("H,D", [(16, 512), (64, 576), (128, 512)])
 @pytest.mark.parametrize("growing", [True, False])
 def test_scores_that_keep_growing(H, D, growing):
