@@ -39,6 +39,10 @@
 
 namespace smla {
 
+#ifndef SMLA_QB_DEPTH
+#define SMLA_QB_DEPTH 1
+#endif
+
 // Split partials are chunks of 4 columns; chunk c (columns 4c .. 4c+3) of the
 // 16 heads of a group sit side by side, so the 16 lanes that hold one chunk of
 // 16 consecutive heads store contiguous bytes.  Index in chunks (8 bytes).
@@ -1121,9 +1125,14 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
 // of PV, so each SIMD interleaves one score wave's and one output wave's MFMAs;
 // three LDS stages hold the tile being scored, the tile being multiplied and
 // the tile being filled, and one barrier per tile separates the phases.
-template <bool KV8, int DQK, bool VL = false>
+template <bool KV8, int DQK, bool VL = false, bool QB = false>
 __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
   using G = Geom<KV8, DQK>;
+  // QB: e4m3 KV with bf16 QK dots (q as given, K widened to bf16 exactly);
+  // F8: e4m3 dots on the quantised q
+  static_assert(!QB || KV8, "bf16 dots are an e4m3-KV variant");
+  constexpr bool F8 = KV8 && !QB;
+  constexpr int NKQ = F8 ? G::NKB : DQK / 32;   // QK k-steps
   constexpr int TR = KV8 ? 64 : 32;        // rows per tile (36 KiB for Dqk = 576 either way)
   constexpr int NB = TR / 16;              // 16-row QK blocks per tile
   constexpr int NKS = TR / 32;             // 32-row PV k-steps per tile
@@ -1265,13 +1274,13 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
 
     // ---- q operand (B of QK^T): lane (head m16, g) holds bf16 columns
     // 32kb + 8g .. +8, or e4m3 codes of columns 128kb + 32g .. +32
-    u32x4 qf[KV8 ? 1 : G::NKB];
-    i32x8 q8[KV8 ? G::NKB : 1];
-    u32x4 qv[KV8 ? G::NKB : 1][4];
-    const bool qpre = KV8 && p.q_scale > 0.0f;   // q given as e4m3 codes
-    if constexpr (!KV8) {
+    u32x4 qf[F8 ? 1 : NKQ];
+    i32x8 q8[F8 ? G::NKB : 1];
+    u32x4 qv[F8 ? G::NKB : 1][4];
+    const bool qpre = F8 && p.q_scale > 0.0f;   // q given as e4m3 codes
+    if constexpr (!F8) {
 #pragma unroll
-      for (int kb = 0; kb < G::NKB; ++kb)
+      for (int kb = 0; kb < NKQ; ++kb)
         qf[kb] = *reinterpret_cast<const u32x4*>(qrow + kb * 32 + 8 * g);
     } else if (qpre) {
       // e4m3 codes of columns 128kb + 32g .. +32 (the B fragment as it is) in
@@ -1301,10 +1310,13 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     // retires them and the loop never waits on them.  e4m3: the rows are
     // requested once q is quantised (fewer registers live at once).
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!KV8) issue(ldA, vmA, vA, 0);
+    if constexpr (!F8) issue(ldA, vmA, vA, 0);
 
     float c2;
-    if constexpr (!KV8) {
+    if constexpr (!F8) {
+      // QB (e4m3 KV): q needs no quantisation, but the output waves still
+      // meet the score waves at the q amax exchange barrier
+      if constexpr (KV8) __syncthreads();
       c2 = p.sm_scale * p.kv_scale * kLog2e;
     } else if (qpre) {
       __syncthreads();   // the output waves' barrier of the q amax exchange
@@ -1373,10 +1385,19 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     // One QK^T A fragment: rows 16b .. 16b + 15 of the tile, bf16 columns
     // 32kb + 8g .. +8 (one 16-byte read) or e4m3 columns 128kb + 32g .. +32
     // (two reads; zeros past Dqk)
-    using Frag = std::conditional_t<KV8, i32x8, u32x4>;
+    using Frag = std::conditional_t<F8, i32x8, u32x4>;
     auto frag = [&](const uint8_t* st, int b, int kb) -> Frag {
       const int r = 16 * b + m16;
-      if constexpr (!KV8) {
+      if constexpr (QB) {
+        // e4m3 columns 32kb + 8g .. +8 (half a 16-byte chunk; RoPE columns from
+        // the tail part), widened to bf16 exactly
+        const int c = 2 * kb + (g >> 1);
+        const int o = (c < G::MCH) ? off_main(r, c) : off_tail(r, c - G::MCH);
+        const u32x2 raw = lds_read8(st + o + 8 * (g & 1));
+        const u32x2 lo = e4m3x4_to_bf16x4(raw[0]);
+        const u32x2 hi = e4m3x4_to_bf16x4(raw[1]);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      } else if constexpr (!KV8) {
         return (kb < G::MCH / 4) ? lds_read16(st + 16 * b * G::MAIN + qk_base[kb & 3] + 256 * (kb >> 2))
                                  : lds_read16(st + off_tail(r, 4 * kb + g - G::MCH));
       } else {
@@ -1397,10 +1418,12 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     // DEPTH k-steps ahead of their MFMA (LDS latency) and each block keeps two
     // partial sums (even / odd k-steps), so back-to-back MFMAs are
     // independent.  e4m3: the four blocks already are.
-    constexpr int DEPTH = 3;
-    constexpr int NACC = 2;
+    // QB: four row blocks are four independent chains already, and its bf16 q
+    // fragments leave fewer registers for reads in flight
+    constexpr int DEPTH = QB ? SMLA_QB_DEPTH : 3;
+    constexpr int NACC = QB ? 1 : 2;
     auto qk = [&](const uint8_t* st, f32x4 (&acc)[NB]) {
-      if constexpr (KV8) {
+      if constexpr (F8) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1419,11 +1442,11 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
 #pragma unroll
           for (int b = 0; b < NB; ++b) ring[d][b] = frag(st, b, d);
 #pragma unroll
-        for (int kb = 0; kb < G::NKB; ++kb) {
+        for (int kb = 0; kb < NKQ; ++kb) {
           Frag cur[NB];
 #pragma unroll
           for (int b = 0; b < NB; ++b) cur[b] = ring[kb % DEPTH][b];
-          if (kb + DEPTH < G::NKB) {
+          if (kb + DEPTH < NKQ) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) ring[kb % DEPTH][b] = frag(st, b, kb + DEPTH);
           }
@@ -1432,7 +1455,7 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
         }
         // issue order: DEPTH k-steps of reads, then one MFMA per read, so
         // NB * DEPTH reads stay in flight (the default schedule keeps ~2)
-        constexpr int NR = NB * G::NKB, PRE = NB * DEPTH;
+        constexpr int NR = NB * NKQ, PRE = NB * DEPTH;
         __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
 #pragma unroll
         for (int i = 0; i < NR - PRE; ++i) {
@@ -1885,9 +1908,7 @@ hipError_t launch_plan(const PlanParams& q, hipStream_t stream) {
 // ---- launch wrappers ----------------------------------------------------------------
 template <bool KV8, int DQK, bool QB>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  // bf16 dots on e4m3 KV run in the 16- and 32-head kernels (64-head groups as
-  // two 32-head groups)
-  const int HT = QB ? (p.H % 32 == 0 ? 32 : 16) : heads_per_workgroup(p.H);
+  const int HT = heads_per_workgroup(p.H);
   const int HG = p.H / HT;
   const int64_t units = p.units ? (int64_t)p.max_units : (int64_t)p.T * p.S;
   const int64_t grid = ((units + 7) / 8) * 8 * HG;
@@ -1915,12 +1936,10 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream, hipEvent_
       hipExtLaunchKernelGGL((smla_tiles_kernel<KV8, DQK, 32, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
       break;
     default:
-      if constexpr (!QB) {
-        if (p.units != nullptr)
-          hipExtLaunchKernelGGL((smla_heads_kernel<KV8, DQK, true>), gd, dim3(2 * kThreads), 0, stream, ev0, ev1, 0, p);
-        else
-          hipExtLaunchKernelGGL((smla_heads_kernel<KV8, DQK, false>), gd, dim3(2 * kThreads), 0, stream, ev0, ev1, 0, p);
-      }
+      if (p.units != nullptr)
+        hipExtLaunchKernelGGL((smla_heads_kernel<KV8, DQK, true, QB>), gd, dim3(2 * kThreads), 0, stream, ev0, ev1, 0, p);
+      else
+        hipExtLaunchKernelGGL((smla_heads_kernel<KV8, DQK, false, QB>), gd, dim3(2 * kThreads), 0, stream, ev0, ev1, 0, p);
       break;
   }
   return hipGetLastError();

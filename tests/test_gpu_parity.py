@@ -429,8 +429,9 @@ BF16_DOT_CASES = [
     (3, 16, 512, 300, 4096, 0.2),     # 16-head kernel
     (2, 16, 576, 257, 2048, 0.1),
     (2, 32, 512, 200, 2048, 0.0),     # 32-head kernel
-    (2, 64, 576, 190, 1024, 0.1),     # 64 heads as two 32-head groups
+    (2, 64, 576, 190, 1024, 0.1),     # 64-head kernel
     (2, 128, 512, 321, 4096, 0.1),
+    (3, 128, 576, 700, 4096, 0.1),    # 64-head kernel, several 64-row tiles per split
 ]
 
 

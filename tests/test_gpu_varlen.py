@@ -93,6 +93,17 @@ def test_varlen_with_sinks_prequantised_q_and_bf16_dots():
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("H,D", [(32, 512), (64, 576), (128, 512)])
+def test_varlen_bf16_dots_in_the_wide_kernels(H, D):
+    T, K = 9, 600
+    case, idx, lens, cut = _mixed_case(T, H, D, K, 4096, "fp8", seed=H + D)
+    out, lse = binding.sparse_mla_fwd_varlen(case.q, case.kv_pool, idx, lens, case.sm_scale, case.kv_scale,
+                                             dot_precision=binding.DOTS_BF16)
+    torch.cuda.synchronize()
+    ref = oracle_for_tokens(case, idx=cut, q_mode=oracle.Q_EXACT)
+    compare(out, lse, ref[0], ref[1], "bf16", f"varlen bf16 dots H{H} D{D}")
+
+
 @pytest.mark.parametrize("H", [16, 64])
 def test_varlen_full_lengths_match_the_padded_call(H):
     # every length = K: the same result as the ordinary call up to summation order
