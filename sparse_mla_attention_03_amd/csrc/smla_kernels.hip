@@ -1047,8 +1047,11 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
 
   // ---- merge the four waves: each writes its raw O (straight from the
   // accumulators) and (max, sum) to LDS; wave w then combines columns
-  // [128w, 128w + 128) of all four in a fixed order and writes them out
+  // [128w, 128w + 128) of all four in a fixed order and writes them out.
+  // Quarter a of O (columns 128a ..) is O[a]; for split partials a wave keeps
+  // its own quarter in registers, so only the other three go through LDS.
   const float l_w = group4_sum(l_run);
+  const UnitTail wt = unit_tail(p, u);
   __syncthreads();   // every wave is done with its slot; the merge reuses them
   float* ob = reinterpret_cast<float*>(smem);
   {
@@ -1057,6 +1060,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
+        if (a == wave && !wt.direct) continue;
         f32x4 v;
 #pragma unroll
         for (int x = 0; x < 4; ++x) { const int j = 4 * k + x; v[x] = O[a][j & 7][j >> 3]; }
@@ -1075,28 +1079,39 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
     f[w] = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][m16] - M);
     Lsum += f[w] * s_l[w][m16];
   }
-  const UnitTail wt = unit_tail(p, u);
   const float2 nz = finish_row(M, Lsum, sink_log2(p, head, wt.direct), p.kv_scale);
   const float scale = nz.x;
   if (!wt.direct) {
-    // 32 chunks x 16 heads of this wave's 128 columns, 8 per lane: store k
-    // takes chunk 32 wave + 4k + g of head m16, so a store covers 1 KB of
-    // consecutive partials
+    // lane (m16, g) merges columns 128 wave + 32 g + 4k .. + 4 (k < 8) of head
+    // m16 -- the columns its own accumulators hold -- and stores them as chunks
+    // 32 wave + 8 g + k: each store writes four whole 128-byte lines
     f32x4 vv[8];
     float amax = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < 4; ++a) {
+      if (a != wave) continue;   // uniform: the quarter index stays a constant
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        v += f[w] * *reinterpret_cast<const f32x4*>(ob + (w * 16 + m16) * OPAD + 128 * wave + 4 * (4 * k + g));
-      vv[k] = v * scale;
-      amax = fmaxf(fmaxf(amax, fmaxf(fabsf(vv[k][0]), fabsf(vv[k][1]))), fmaxf(fabsf(vv[k][2]), fabsf(vv[k][3])));
+      for (int k = 0; k < 8; ++k) {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          f32x4 o;
+          if (w == a) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) { const int j = 4 * k + x; o[x] = O[a][j & 7][j >> 3]; }
+          } else {
+            o = *reinterpret_cast<const f32x4*>(ob + (w * 16 + m16) * OPAD + 128 * a + 32 * g + 4 * k);
+          }
+          v += f[w] * o;
+        }
+        vv[k] = v * scale;
+        amax = fmaxf(fmaxf(amax, fmaxf(fabsf(vv[k][0]), fabsf(vv[k][1]))), fmaxf(fabsf(vv[k][2]), fabsf(vv[k][3])));
+      }
     }
     const int e = part_exp(quarter_max(amax));   // this wave's columns are quarter `wave`
-    u32x2* dst = reinterpret_cast<u32x2*>(p.part_o) + part_chunk(p, wt.prow, head, 32 * wave + g);
+    u32x2* dst = reinterpret_cast<u32x2*>(p.part_o) + part_chunk(p, wt.prow, head, 32 * wave + 8 * g);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) part_store(dst + 64 * k, part_encode(vv[k], e));
+    for (int k = 0; k < 8; ++k) part_store(dst + 16 * k, part_encode(vv[k], e));
     if (g == 0) part_store_scale(p, wt.prow, head, wave, e);
   } else {
     // 16 heads x 16 chunks of 8 columns, 4 per lane: store k takes head 4k + g,
