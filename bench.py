@@ -58,6 +58,11 @@ def parse():
                          "(FETCH_SIZE / WRITE_SIZE of this workload, then of --copy-calibration "
                          "--copy-bytes) into profiles/traffic_<workload>.json")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--sensitivity", action="store_true",
+                    help="also time (not part of value): each call after a 1 GiB read that "
+                         "evicts the caches (cold; for prefill this is the cold first call), "
+                         "the same workload with every top-k list sorted by slot, and with "
+                         "block size 1 (every position its own randomly placed slot)")
     return ap.parse_args()
 
 
@@ -167,6 +172,85 @@ def traffic_summary(workload: str, dirs, copy_bytes: int) -> None:
     with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec), flush=True)
+
+
+def graph_us_per_call(call, steps: int) -> float:
+    """Median over BATCHES graph replays of `steps` captured calls, per call."""
+    import numpy as np
+    import torch
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            call(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(BATCHES):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms.append(t0.elapsed_time(t1))
+    del graph
+    return float(np.median(ms)) / steps * 1e3
+
+
+def sensitivity(spec, cases, call_case, steps: int) -> dict:
+    """Timings that are not the workload (reported beside it): cold caches, lists
+    sorted by slot, block size 1."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_03_amd import synth
+    res = {}
+    # cold: a 1 GiB read between calls evicts L2 and the 256 MB Infinity Cache
+    # (a read, so the caches hold clean lines: a write would leave dirty ones
+    # whose write-back the call would pay for); only the call is timed (events
+    # on the current stream, eager calls)
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    sink = torch.empty((), dtype=torch.float32, device="cuda:0")
+    times = []
+    for i in range(20):
+        torch.sum(scratch, dim=0, out=sink)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        call_case(cases[i % len(cases)])
+        t1.record()
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1) * 1e3)
+    res["cold_first_call_us"] = round(times[0], 3)
+    res["cold_us_median"] = round(float(np.median(times)), 3)
+    del scratch
+    # every list sorted by slot (padding first): same rows, better locality
+    srt = []
+    for c in cases:
+        idx = torch.sort(c.topk_idx, dim=1).values.contiguous()
+        srt.append(dataclasses.replace(c, topk_idx=idx))
+    res["sorted_lists_us"] = round(graph_us_per_call(lambda i: call_case(srt[i % len(srt)]), steps), 3)
+    del srt
+    # block size 1: every logical position is its own randomly placed slot
+    spec1 = dataclasses.replace(spec, block_size=1)
+    c1 = synth.make_case(spec1, device="cuda:0", index_sets=len(cases))
+    c1 = c1 if isinstance(c1, list) else [c1]
+    res["block_size_1_us"] = round(graph_us_per_call(lambda i: call_case(c1[i % len(c1)]), steps), 3)
+    del c1
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(cases, budget_s: float):
@@ -495,6 +579,12 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cases, args.cpu_seconds)
+    sens = None
+    if args.sensitivity:
+        def call_case(c):
+            sparse_mla_fwd_ex(c.q, c.kv_pool, c.topk_idx, c.sm_scale, c.kv_scale, out=out, lse=lse,
+                              workspace=ws, num_splits=0)
+        sens = sensitivity(spec, cases, call_case, args.steps)
 
     line = {
         "metric": "sparse-MLA decode \u00b5s/call + gathered-KV HBM GB/s; prefill TFLOP/s (1 MI355X)",
@@ -521,6 +611,8 @@ def main():
         "batch_ms": [round(b, 4) for b in batch_ms],
         "wall_s": round(wall, 3),
     }
+    if sens is not None:
+        line["sensitivity"] = sens
     print(json.dumps(line), flush=True)
 
 
