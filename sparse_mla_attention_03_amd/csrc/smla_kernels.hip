@@ -186,6 +186,18 @@ __device__ __forceinline__ int lds_tail(int r, int c) {
 __device__ __forceinline__ u32x4 lds_read16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane k reads 4 consecutive
+// 16-bit values D_k[0..3] at its address, and lane 4a + b receives
+// D_{a + 4j}[b] for j = 0..3 (a 16 x 4 block read row-wise, delivered
+// column-wise).  With lane k of a group reading row k / 4 of a 4-row block at
+// column offset c_{k % 4}, lane i gets column c_{i / 4} + i % 4 of all 4 rows:
+// the k-major MFMA operand of a row-major tile.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+  typedef __attribute__((ext_vector_type(4))) short s16x4;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
 __device__ __forceinline__ u32x2 lds_read8(const uint8_t* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }
@@ -826,6 +838,20 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   int pv_base[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) pv_base[i] = (4 * g + i) * G::MAIN + 16 * (m16 ^ row_key(4 * g + i));
+  // bf16 V through transposed LDS reads: in k-slot group g, lane k = m16 of the
+  // group reads row 16b + 4g + (k >> 2) (key kr), 4 columns from
+  // 128a + 32 (k & 3) + 4e; 16-byte chunk 16a + 4 (k & 3) + (e >> 1) of that
+  // row lands at 16a + ((4 (k & 3) + (e >> 1)) ^ kr), half e & 1 of it.  So
+  // lane (m16, g) receives column 128a + 32 (m16 >> 2) + 4e + (m16 & 3) of
+  // rows 16b + 4g .. + 3, the A operand whose output lane (head, g) holds
+  // columns 128a + 32g + 4e + i in O[a][e][i].
+  int pvt_base[NB][4];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int r = 16 * b + 4 * g + (m16 >> 2);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) pvt_base[b][h] = r * G::MAIN + 16 * ((4 * (m16 & 3) + h) ^ row_key(r));
+  }
 
   f32x4 O[4][8];
 #pragma unroll
@@ -973,6 +999,27 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
       pk[b][0] = pack_bf16(e0, e1);
       pk[b][1] = pack_bf16(e2, e3);
     }
+    if constexpr (!KV8) {
+      // per 128-column chunk a: the 8 NB transposed reads first, then the 8 MFMAs
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        u32x2 A[8][NB];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) A[e][b] = lds_read_tr16(slot + pvt_base[b][e >> 1] + 256 * a + 8 * (e & 1));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (NB == 1) {
+            O[a][e] = mfma_bf16_k16(A[e][0], u32x2{pk[0][0], pk[0][1]}, O[a][e]);
+          } else {
+            O[a][e] = mfma_bf16(u32x4{A[e][0][0], A[e][0][1], A[e][1][0], A[e][1][1]},
+                                u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]}, O[a][e]);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int c = m16 + 16 * a;   // 8-column chunk of this lane
@@ -1050,6 +1097,19 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   // [128w, 128w + 128) of all four in a fixed order and writes them out.
   // Quarter a of O (columns 128a ..) is O[a]; for split partials a wave keeps
   // its own quarter in registers, so only the other three go through LDS.
+  // columns 128a + 32g + 4k .. + 3 of this lane's head: one accumulator with
+  // bf16 V (transposed reads), spread over four with e4m3 V (column 8c + e of
+  // chunk c in O[a][e])
+  auto o_quad = [&](int a, int k) -> f32x4 {
+    if constexpr (!KV8) {
+      return O[a][k];
+    } else {
+      f32x4 v;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) { const int j = 4 * k + x; v[x] = O[a][j & 7][j >> 3]; }
+      return v;
+    }
+  };
   const float l_w = group4_sum(l_run);
   const UnitTail wt = unit_tail(p, u);
   __syncthreads();   // every wave is done with its slot; the merge reuses them
@@ -1061,10 +1121,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         if (a == wave && !wt.direct) continue;
-        f32x4 v;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) { const int j = 4 * k + x; v[x] = O[a][j & 7][j >> 3]; }
-        *reinterpret_cast<f32x4*>(row + 128 * a + 32 * g + 4 * k) = v;
+        *reinterpret_cast<f32x4*>(row + 128 * a + 32 * g + 4 * k) = o_quad(a, k);
       }
   }
   if (g == 0) { s_m[wave][m16] = m_run; s_l[wave][m16] = l_w; }
@@ -1097,8 +1154,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
         for (int w = 0; w < 4; ++w) {
           f32x4 o;
           if (w == a) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) { const int j = 4 * k + x; o[x] = O[a][j & 7][j >> 3]; }
+            o = o_quad(a, k);
           } else {
             o = *reinterpret_cast<const f32x4*>(ob + (w * 16 + m16) * OPAD + 128 * a + 32 * g + 4 * k);
           }
