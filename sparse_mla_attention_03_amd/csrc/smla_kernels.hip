@@ -909,7 +909,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
                    (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
     }
   };
-  constexpr int DEPTH = 2;
+  constexpr int DEPTH = 3;
   auto qk = [&](f32x4 (&acc)[NB]) {
     if constexpr (F8) {
       // e4m3: few, wide k-steps (128 columns); the NB blocks are the
