@@ -1000,24 +1000,37 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
       pk[b][1] = pack_bf16(e2, e3);
     }
     if constexpr (!KV8) {
-      // per 128-column chunk a: the 8 NB transposed reads first, then the 8 MFMAs
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        u32x2 A[8][NB];
+      // 128-column chunk a + 1's transposed reads interleaved with chunk a's MFMAs
+      u32x2 A[2][8][NB];
+      auto load_a = [&](int a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
 #pragma unroll
-          for (int b = 0; b < NB; ++b) A[e][b] = lds_read_tr16(slot + pvt_base[b][e >> 1] + 256 * a + 8 * (e & 1));
+          for (int b = 0; b < NB; ++b) A[a & 1][e][b] = lds_read_tr16(slot + pvt_base[b][e >> 1] + 256 * a + 8 * (e & 1));
+      };
+      load_a(0);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        if (a + 1 < 4) load_a(a + 1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           if constexpr (NB == 1) {
-            O[a][e] = mfma_bf16_k16(A[e][0], u32x2{pk[0][0], pk[0][1]}, O[a][e]);
+            O[a][e] = mfma_bf16_k16(A[a & 1][e][0], u32x2{pk[0][0], pk[0][1]}, O[a][e]);
           } else {
-            O[a][e] = mfma_bf16(u32x4{A[e][0][0], A[e][0][1], A[e][1][0], A[e][1][1]},
+            O[a][e] = mfma_bf16(u32x4{A[a & 1][e][0][0], A[a & 1][e][0][1], A[a & 1][e][1][0], A[a & 1][e][1][1]},
                                 u32x4{pk[0][0], pk[0][1], pk[1][0], pk[1][1]}, O[a][e]);
           }
         }
       }
+      // issue order: chunk 0's reads, then per chunk its MFMAs with the next chunk's reads between them
+      __builtin_amdgcn_sched_group_barrier(0x100, 8 * NB, 0);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (a + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);
+        }
       return;
     }
 #pragma unroll
