@@ -291,7 +291,23 @@ def cpu_baseline(cases, budget_s: float):
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{n_calls} whole calls of the same workload ({n_tok} query tokens, "
                       f"fp64 C oracle, OpenMP over (token, head)), {t_total:.1f} s",
-            "us_per_call": round(t_total / n_calls * 1e6, 1)}
+            "us_per_call": round(t_total / n_calls * 1e6, 1)}, staged
+
+
+def cpu_single_thread(staged) -> dict:
+    """The same oracle on one host thread: one whole call of the workload."""
+    import oracle
+    threads = oracle.num_threads()
+    q, kv, remap, nbytes, case = staged[0]
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.sparse_mla_fwd(q, kv, remap, case.sm_scale, case.kv_scale)
+        dt = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": round(nbytes / dt / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "one whole call of the same workload on one thread", "us_per_call": round(dt * 1e6, 1)}
 
 
 # The fused q-RoPE / q-concat / KV-concat / cache write (the step in front of the
@@ -576,9 +592,10 @@ def main():
                     "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                     "traffic": traffic}
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cases, args.cpu_seconds)
+        cpu, staged = cpu_baseline(cases, args.cpu_seconds)
+        cpu1 = cpu_single_thread(staged)
     sens = None
     if args.sensitivity:
         def call_case(c):
@@ -608,6 +625,7 @@ def main():
         "roofline": roofline,
         "main_kernel_us": round(kern_avg_ms * 1e3, 3),
         "cpu_baseline": cpu,
+        "cpu_baseline_1_thread": cpu1,
         "batch_ms": [round(b, 4) for b in batch_ms],
         "wall_s": round(wall, 3),
     }

@@ -77,12 +77,19 @@ def _load():
         c_p, ctypes.c_int, ctypes.c_double, c_p, c_p, ctypes.c_int, c_i64, ctypes.c_double]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_num_threads.restype = None
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's following calls use."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def bf16_value(bits) -> np.ndarray:

@@ -92,6 +92,14 @@ void oracle_quantize_q_tiles(const uint16_t* q, int64_t T, int64_t H, int64_t Dq
 
 /* ---- the forward pass --------------------------------------------------- */
 
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -116,6 +116,8 @@ int oracle_rope_concat_cache(const uint16_t* ql_nope, int64_t ql_st, int64_t ql_
 
 /* Number of OpenMP threads the oracle will use (1 when built without it). */
 int oracle_num_threads(void);
+/* threads the following calls use (OpenMP; the default is the host's count) */
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
