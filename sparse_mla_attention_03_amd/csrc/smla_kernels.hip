@@ -845,12 +845,25 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   // lane (m16, g) receives column 128a + 32 (m16 >> 2) + 4e + (m16 & 3) of
   // rows 16b + 4g .. + 3, the A operand whose output lane (head, g) holds
   // columns 128a + 32g + 4e + i in O[a][e][i].
-  int pvt_base[NB][4];
+  // 32-row tiles: lanes with k & 2 set read the other 8-byte half of each
+  // 16-byte chunk (columns from 4 (e ^ 1)): lanes (k & 3, row) and
+  // (k & 3 ^ 2, row ^ 1) of a group land on the same 16-byte bank slot of the
+  // swizzle and so use different halves of it (a third of the bank-conflict
+  // cycles on prefill; the 16-row decode tiles keep the plain order, where the
+  // extra lane arithmetic costs more than the conflicts).  O[a][e] of output
+  // lane group g then holds columns 128a + 32g + 4 (e ^ ((g >> 1) & 1)).
+  constexpr bool FLIP = !KV8 && TR == 32;
+  int pvt_base[NB][4][2];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int r = 16 * b + 4 * g + (m16 >> 2);
+    const int fl = FLIP ? 8 * ((m16 >> 1) & 1) : 0;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) pvt_base[b][h] = r * G::MAIN + 16 * ((4 * (m16 & 3) + h) ^ row_key(r));
+    for (int h = 0; h < 4; ++h) {
+      const int base = r * G::MAIN + 16 * ((4 * (m16 & 3) + h) ^ row_key(r));
+      pvt_base[b][h][0] = base + fl;
+      pvt_base[b][h][1] = base + 8 - fl;
+    }
   }
 
   f32x4 O[4][8];
@@ -1006,7 +1019,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
 #pragma unroll
-          for (int b = 0; b < NB; ++b) A[a & 1][e][b] = lds_read_tr16(slot + pvt_base[b][e >> 1] + 256 * a + 8 * (e & 1));
+          for (int b = 0; b < NB; ++b) A[a & 1][e][b] = lds_read_tr16(slot + pvt_base[b][e >> 1][e & 1] + 256 * a);
       };
       load_a(0);
 #pragma unroll
@@ -1110,9 +1123,10 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   // [128w, 128w + 128) of all four in a fixed order and writes them out.
   // Quarter a of O (columns 128a ..) is O[a]; for split partials a wave keeps
   // its own quarter in registers, so only the other three go through LDS.
-  // columns 128a + 32g + 4k .. + 3 of this lane's head: one accumulator with
-  // bf16 V (transposed reads), spread over four with e4m3 V (column 8c + e of
-  // chunk c in O[a][e])
+  // quad k of this lane's head in quarter a: columns 128a + 32g + 4 (k ^ fq)
+  // .. + 3; one accumulator with bf16 V (transposed reads), spread over four
+  // with e4m3 V (column 8c + e of chunk c in O[a][e]; fq = 0)
+  const int fq = FLIP ? ((g >> 1) & 1) : 0;
   auto o_quad = [&](int a, int k) -> f32x4 {
     if constexpr (!KV8) {
       return O[a][k];
@@ -1134,7 +1148,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         if (a == wave && !wt.direct) continue;
-        *reinterpret_cast<f32x4*>(row + 128 * a + 32 * g + 4 * k) = o_quad(a, k);
+        *reinterpret_cast<f32x4*>(row + 128 * a + 32 * g + 4 * (k ^ fq)) = o_quad(a, k);
       }
   }
   if (g == 0) { s_m[wave][m16] = m_run; s_l[wave][m16] = l_w; }
@@ -1152,9 +1166,9 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   const float2 nz = finish_row(M, Lsum, sink_log2(p, head, wt.direct), p.kv_scale);
   const float scale = nz.x;
   if (!wt.direct) {
-    // lane (m16, g) merges columns 128 wave + 32 g + 4k .. + 4 (k < 8) of head
-    // m16 -- the columns its own accumulators hold -- and stores them as chunks
-    // 32 wave + 8 g + k: each store writes four whole 128-byte lines
+    // lane (m16, g) merges columns 128 wave + 32 g + 4 (k ^ fq) .. + 4 (k < 8) of
+    // head m16 -- the columns its own accumulators hold -- and stores them as
+    // chunks 32 wave + 8 g + (k ^ fq): each store writes four whole 128-byte lines
     f32x4 vv[8];
     float amax = 0.0f;
 #pragma unroll
@@ -1169,7 +1183,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
           if (w == a) {
             o = o_quad(a, k);
           } else {
-            o = *reinterpret_cast<const f32x4*>(ob + (w * 16 + m16) * OPAD + 128 * a + 32 * g + 4 * k);
+            o = *reinterpret_cast<const f32x4*>(ob + (w * 16 + m16) * OPAD + 128 * a + 32 * g + 4 * (k ^ fq));
           }
           v += f[w] * o;
         }
@@ -1180,7 +1194,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
     const int e = part_exp(quarter_max(amax));   // this wave's columns are quarter `wave`
     u32x2* dst = reinterpret_cast<u32x2*>(p.part_o) + part_chunk(p, wt.prow, head, 32 * wave + 8 * g);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) part_store(dst + 16 * k, part_encode(vv[k], e));
+    for (int k = 0; k < 8; ++k) part_store(dst + 16 * (k ^ fq), part_encode(vv[k], e));
     if (g == 0) part_store_scale(p, wt.prow, head, wave, e);
   } else {
     // 16 heads x 16 chunks of 8 columns, 4 per lane: store k takes head 4k + g,
