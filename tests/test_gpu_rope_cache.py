@@ -6,6 +6,8 @@ scales, skipped slots and a strided (heads-outermost) ql_nope.
 """
 from __future__ import annotations
 
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -112,3 +114,53 @@ def test_fused_outputs_feed_the_forward_pass():
                                              q_mode=oracle.Q_GIVEN_FP8, q_scale=q_scale)
     assert np.max(np.abs(out.float().cpu().numpy() - ref_out)) <= 6e-2
     assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= 1e-3
+
+
+# bf16 bit patterns of the edge-value test: zeros, small integers, the largest
+# finite bf16, the smallest normal one and 2^-100 (so that products reach the
+# subnormal range), and a value one step above 1
+_EDGE_BF16 = np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x4000, 0xC000, 0x4040, 0x3F81, 0x0D80, 0x0080,
+                       0x7F7F, 0xFF7F, 0x3F00], dtype=np.uint16)
+
+
+def _edge_table():
+    """A rotary table whose rows are chosen so that outputs land on the cases the
+    bf16 rounding has to get right: exact bf16 midpoints with a tiny second
+    product pushing them either way (or not at all), subnormal and underflowing
+    outputs, overflow to infinity, exact zeros, and plain angles."""
+    cs = np.empty((8, 64), np.float32)
+    rows = [(1.0, 0.0), (0.5 + 2.0 ** -9, 2.0 ** -40), (2.0 ** -30, 2.0 ** -31), (0.75, 0.75),
+            None, (1.0 - 2.0 ** -24, 2.0 ** -12), (0.0, 1.0), (0.999, -0.0447)]
+    real = synth.rope_cos_sin(4096)[1234]
+    for p, r in enumerate(rows):
+        if r is None:
+            cs[p] = real
+        else:
+            cs[p, :32], cs[p, 32:] = r
+    return cs
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+@pytest.mark.parametrize("q_fp8,kv_fp8", [(False, False), (True, True)])
+def test_fused_rope_cache_rounding_edge_values(is_neox, q_fp8, kv_fp8):
+    T, H = 64, 16
+    case = synth.make_rope_case(T=T, H=H, num_blocks=2, block_size=64, seed=31)
+    rng = np.random.default_rng(32)
+
+    def edge(shape):
+        bits = _EDGE_BF16[rng.integers(0, len(_EDGE_BF16), size=shape)]
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+
+    case = replace(case, q_pe=edge((T, H, 64)), k_pe=edge((T, 64)),
+                   positions=torch.arange(T, dtype=torch.int64) % 8,
+                   cos_sin=torch.from_numpy(_edge_table()))
+    _check(case, is_neox, q_fp8, kv_fp8, q_scale=1.0, kv_scale=1.0)
+
+
+@pytest.mark.parametrize("q_fp8,kv_fp8", [(False, False), (True, True)])
+def test_fused_rope_cache_large_call(q_fp8, kv_fp8):
+    # 2900 tokens x 17 rows = 49300 rows: past the size from which the kernel
+    # interleaves its two kinds of wave, with a ragged last group
+    case = synth.make_rope_case(T=2900, H=16, num_blocks=64, block_size=64, max_pos=8192, seed=41,
+                                skip_frac=0.05)
+    _check(case, True, q_fp8, kv_fp8, q_scale=0.37, kv_scale=0.59)
