@@ -94,12 +94,16 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
+# the sources of the forward pass's kernels and their launch configuration; the
+# fused RoPE / cache write is a kernel of its own and does not enter the hash
+FWD_SOURCES = ("smla_api.hip", "smla_device.h", "smla_kernels.h", "smla_kernels.hip")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_mla_attention_03_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in FWD_SOURCES:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 

@@ -90,3 +90,10 @@ def test_missing_counter_rows_are_an_error(tmp_path):
 def test_kernel_source_hash_is_stable():
     assert bench.kernel_source_hash() == bench.kernel_source_hash()
     assert len(bench.kernel_source_hash()) == 16
+
+
+def test_kernel_source_hash_covers_the_forward_sources():
+    csrc = os.path.join(ROOT, "sparse_mla_attention_03_amd", "csrc")
+    listed = {f for f in os.listdir(csrc) if f.endswith((".hip", ".h"))}
+    # every source except the fused RoPE / cache write's own file
+    assert set(bench.FWD_SOURCES) == listed - {"smla_rope_cache.hip"}
