@@ -23,8 +23,9 @@
 // rounded once to bf16 on the fp64 bits; a chunk with an output outside the
 // range of normal bf16 numbers (zero, subnormal, non-finite) takes a two-step
 // conversion instead (to fp32 with round-to-odd, which keeps the final
-// round-to-nearest-even exact).  e4m3 outputs encode value / scale (IEEE fp32
-// division, saturated to +-448, round to nearest even) of the bf16 value.
+// round-to-nearest-even exact).  e4m3 outputs encode value / scale (the
+// correctly rounded fp32 quotient, saturated to +-448, round to nearest even)
+// of the bf16 value.
 #include <hip/hip_runtime.h>
 
 #include "smla_device.h"
@@ -68,6 +69,22 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne_normal(double d, bool& ok) {
   return ((t >> 16) & 0x8000u) | (((t >> 13) & 0x3ffffu) - ((1023u - 127u) << 7));
 }
 
+// v / s rounded to nearest fp32 without a division per value, given
+// r = RN(1 / s) with 2^-64 <= s <= 2^64: q0 = RN(v r) lies within an ulp of
+// the quotient, so the residual v - q0 s is exact in one fma and one more fma
+// q0 + residual * r rounds to RN(v / s) (Markstein's correction step), while
+// no intermediate underflows -- which holds wherever the e4m3 code depends on
+// the exact quotient (|v / s| >= 2^-11, so |v| >= 2^-75).  Smaller quotients
+// only need their sign and to stay below 2^-10 (code +-0), which the
+// copysign keeps for zeros too; when q0 is past 1024 (or infinite) it is used
+// as it is, since it saturates like the quotient.
+__device__ __forceinline__ float quotient_rn(float v, float s, float r) {
+  const float q0 = v * r;
+  const float e = __builtin_fmaf(-q0, s, v);
+  const float q1 = __builtin_fmaf(e, r, q0);
+  return __builtin_copysignf(fabsf(q0) > 1024.0f ? q0 : q1, v);
+}
+
 // eight outputs (as fp32 values of bf16 numbers) -> their encoding at dst
 template <bool E4M3>
 __device__ __forceinline__ void store8(uint8_t* dst, const float (&v)[8], float scale) {
@@ -76,8 +93,16 @@ __device__ __forceinline__ void store8(uint8_t* dst, const float (&v)[8], float 
         u32x4{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
   } else {
     float y[8];
+    if (scale >= 0x1p-64f && scale <= 0x1p64f) {   // uniform
+      const float r = 1.0f / scale;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(v[i] / scale, -kE4m3Max), kE4m3Max);
+      for (int i = 0; i < 8; ++i) y[i] = quotient_rn(v[i], scale, r);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = v[i] / scale;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(y[i], -kE4m3Max), kE4m3Max);
     *reinterpret_cast<u32x2*>(dst) =
         u32x2{f32x4_to_e4m3x4(y[0], y[1], y[2], y[3]), f32x4_to_e4m3x4(y[4], y[5], y[6], y[7])};
   }

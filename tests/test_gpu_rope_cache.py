@@ -164,3 +164,25 @@ def test_fused_rope_cache_large_call(q_fp8, kv_fp8):
     case = synth.make_rope_case(T=2900, H=16, num_blocks=64, block_size=64, max_pos=8192, seed=41,
                                 skip_frac=0.05)
     _check(case, True, q_fp8, kv_fp8, q_scale=0.37, kv_scale=0.59)
+
+
+@pytest.mark.parametrize("scale", [0.37, 1.0, 3.0, 1.0000001, 2.0 ** -64, 2.0 ** 64, 2.0 ** -65, 2.0 ** 65])
+def test_fused_rope_cache_e4m3_every_bf16_input(scale):
+    """Every finite and infinite bf16 pattern as a latent input of a q row and of a
+    cache row, quantised to e4m3 against scales inside, at the ends of and
+    outside the range where the kernel forms value / scale without a division.
+    (NaN patterns are replaced by zero: NaN inputs are outside what the op
+    defines.)"""
+    T, H = 128, 1
+    case = synth.make_rope_case(T=T, H=H, num_blocks=4, block_size=64, seed=51)
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    nan = ((bits & 0x7F80) == 0x7F80) & ((bits & 0x7F) != 0)
+    bits[nan] = 0
+    rng = np.random.default_rng(52)
+    q_bits, kv_bits = rng.permutation(bits), rng.permutation(bits)
+
+    def bf(b, shape):
+        return torch.from_numpy(b.view(np.int16).reshape(shape).copy()).view(torch.bfloat16)
+
+    case = replace(case, ql_nope=bf(q_bits, (T, H, 512)), kv_c=bf(kv_bits, (T, 512)))
+    _check(case, True, True, True, q_scale=scale, kv_scale=scale)
