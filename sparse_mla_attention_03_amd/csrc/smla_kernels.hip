@@ -2032,9 +2032,11 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream, hipEvent_
       // take 16-row wave tiles -- more, shorter pipeline stages and a shorter
       // tail after the last gather.  Whole lists (prefill, bound by LDS
       // bandwidth) take 32-row tiles where four of them plus q fit in LDS: one
-      // q fragment read then feeds two 16-row blocks.
+      // q fragment read then feeds two 16-row blocks -- unless the list is so
+      // short that each wave would get a single 32-row tile, with nothing to
+      // overlap its gather (K <= 128: 16-row tiles measured 2 - 3 % faster).
       if constexpr (KV8 || DQK == 512) {
-        if (p.S > 1 || p.units != nullptr)
+        if (p.S > 1 || p.units != nullptr || p.K <= 4 * 32)
           hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 16, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
         else
           hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 32, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);
