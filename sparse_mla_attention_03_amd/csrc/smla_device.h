@@ -77,12 +77,6 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
 }
 
 // ---- buffer loads ---------------------------------------------------------------
-// Structured buffer: record i of `stride` bytes at base + i*stride.  A record
-// index >= num_records is out of range: the load returns zeros and touches no
-// memory, which is how padding entries of a top-k list are gathered.
-__device__ u32x4 struct_load_b128(__amdgpu_buffer_rsrc_t rsrc, int vindex, int voffset, int soffset,
-                                  int aux) __asm("llvm.amdgcn.struct.ptr.buffer.load.v4i32");
-
 // Raw buffer: byte offset voffset from the base; offsets at or past
 // num_records bytes read zero.
 __device__ int raw_load_b32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)

@@ -157,6 +157,15 @@ __device__ __forceinline__ float2 finish_row(float m, float l, float s2, float k
 // Stand-in for the rows of invalid top-k entries: all zero, never written.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[2048];
 
+// Address of pool row `rec` (rec < 0: the zero row).  The byte offset is
+// formed in 64 bits: a structured buffer (record index x stride) wraps its
+// offset at 2^32 bytes, which would silently gather the wrong rows of a pool
+// larger than 4 GiB.
+__device__ __forceinline__ const uint8_t* pool_row(const uint8_t* kv, int rec, int row_bytes) {
+  return rec >= 0 ? kv + (int64_t)rec * row_bytes : g_zero_row;
+}
+__device__ __forceinline__ u32x4 load16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
 template <bool KV8, int DQK>
 struct Geom {
   static constexpr int ELEM = KV8 ? 1 : 2;
@@ -671,11 +680,6 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   const uint16_t* qtok = p.q + (int64_t)t * p.q_st;
   const int32_t* idx_t = p.idx + (int64_t)t * p.idx_st;
 
-  // the pool as a structured buffer of N rows: out-of-range indices read zeros
-  const uint32_t nrec = (uint32_t)min(p.N, (int64_t)0xffffffffLL);
-  const __amdgpu_buffer_rsrc_t pool =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, (short)G::ROW, (int)nrec, kBufferRsrcWord3);
-
   uint8_t* slot = smem + wave * WSLOT;   // this wave's tile, rows 0 .. TR-1
   // 16-byte chunk c of tile row r sits at chunk position c ^ row_key(r) (V
   // part) or c ^ (r & (TCH-1)) (RoPE part): conflict-free row and column accesses.
@@ -693,20 +697,19 @@ __global__ __launch_bounds__(kThreads, 1) void smla_rows_kernel(FwdParams p) {
   auto issue = [&](u32x4 (&ld)[NLD], uint32_t& vmask, int vslot) {
     const bool ok = lane < TR && vslot >= 0 && (int64_t)vslot < p.N;
     vmask = (uint32_t)__ballot(ok);
-    const int rec = ok ? vslot : -1;   // -1 = 0xffffffff >= any record count
+    const int rec = ok ? vslot : -1;   // -1: the zero row
 #pragma unroll
     for (int grp = 0; grp < NGRP; ++grp) {
-      const int ri = __shfl(rec, 8 * grp + (lane >> 3));
+      const uint8_t* rp = pool_row(p.kv, __shfl(rec, 8 * grp + (lane >> 3)), G::ROW) + 16 * (lane & 7);
 #pragma unroll
-      for (int i = 0; i < NCI; ++i)
-        ld[grp * NCI + i] = struct_load_b128(pool, ri, 16 * (lane & 7) + 128 * i, 0, 0);
+      for (int i = 0; i < NCI; ++i) ld[grp * NCI + i] = load16(rp + 128 * i);
     }
     if constexpr (NLDT > 0) {
       // RoPE part: 8 rows x 8 chunks (bf16) or 16 rows x 4 chunks (e4m3) per load
 #pragma unroll
       for (int j = 0; j < NLDT; ++j) {
-        const int ri = __shfl(rec, TROWS * j + lane / G::TCH);
-        ld[NLDM + j] = struct_load_b128(pool, ri, G::MAIN + 16 * (lane % G::TCH), 0, 0);
+        const uint8_t* rp = pool_row(p.kv, __shfl(rec, TROWS * j + lane / G::TCH), G::ROW);
+        ld[NLDM + j] = load16(rp + G::MAIN + 16 * (lane % G::TCH));
       }
     }
   };
@@ -1313,9 +1316,6 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     const int head = h0 + 16 * qw + m16;
     const uint16_t* qrow = qtok + (int64_t)head * p.q_sh;
     const int32_t* idx_t = p.idx + (int64_t)t * p.idx_st;
-    const uint32_t nrec = (uint32_t)min(p.N, (int64_t)0xffffffffLL);
-    const __amdgpu_buffer_rsrc_t pool =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.kv, (short)G::ROW, (int)nrec, kBufferRsrcWord3);
 
     // slot ids through a raw buffer over this split's entries: the load is
     // issued for every lane (out of range reads zero), then masked to -1
@@ -1332,19 +1332,18 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
       const int k = kbeg + TR * j + RPW * qw + (lane & (RPW - 1));
       const bool ok = lane < RPW && k < kend && vslot >= 0 && (int64_t)vslot < p.N;
       vm = (uint32_t)__ballot(ok);
-      const int rec = ok ? vslot : -1;
+      const int rec = ok ? vslot : -1;   // -1: the zero row
 #pragma unroll
       for (int grp = 0; grp < NGRP; ++grp) {
-        const int ri = __shfl(rec, 8 * grp + (lane >> 3));
+        const uint8_t* rp = pool_row(p.kv, __shfl(rec, 8 * grp + (lane >> 3)), G::ROW) + 16 * (lane & 7);
 #pragma unroll
-        for (int i = 0; i < NCI; ++i)
-          ld[grp * NCI + i] = struct_load_b128(pool, ri, 16 * (lane & 7) + 128 * i, 0, 0);
+        for (int i = 0; i < NCI; ++i) ld[grp * NCI + i] = load16(rp + 128 * i);
       }
       if constexpr (NLDT > 0) {
 #pragma unroll
         for (int j = 0; j < NLDT; ++j) {
-          const int ri = __shfl(rec, TROWS * j + lane / G::TCH);
-          ld[NLDM + j] = struct_load_b128(pool, ri, G::MAIN + 16 * (lane % G::TCH), 0, 0);
+          const uint8_t* rp = pool_row(p.kv, __shfl(rec, TROWS * j + lane / G::TCH), G::ROW);
+          ld[NLDM + j] = load16(rp + G::MAIN + 16 * (lane % G::TCH));
         }
       }
     };

@@ -338,17 +338,73 @@ FULL = ["tiny_bf16", "decode_bf16", "decode_fp8", "rope_decode_bf16", "rope_deco
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_parity(name):
+def test_full_size_parity(name):
+    """Every token (decode) and every query row (prefill) of the workload at its
+    full size, in the launch configuration the benchmark times (automatic
+    split), against the oracle."""
     spec = synth.CONFIGS[name]
+    print(f"full-size parity {name}", flush=True)
     case = synth.make_case(spec, device=DEV)
-    out, lse = run(case)                                  # automatic split, as benchmarked
-    T = spec.T
-    tokens = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(0).choice(T, min(T, 6),
-                                                                                  replace=False)]))
-    ref_out, ref_lse = oracle_for_tokens(case, tokens=tokens)
-    compare(out[torch.from_numpy(tokens).to(DEV)], lse[torch.from_numpy(tokens).to(DEV)],
-            ref_out, ref_lse, spec.kv_dtype, name)
+    out, lse = run(case)
+    ref_out, ref_lse = oracle_for_tokens(case)
+    compare(out, lse, ref_out, ref_lse, spec.kv_dtype, name)
     del case
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- pools past 4 GiB
+
+# (H, Dqk, kv, tokens, context per token): every pool is larger than 2^32 bytes,
+# and its rows past byte 2^32 are named by the lists
+BIG_POOLS = [
+    (16, 576, "bf16", 8, 1 << 19),     # 4,194,304 rows of 1152 B: 4.83 GB
+    (128, 576, "bf16", 8, 1 << 19),
+    (16, 512, "fp8", 8, 9 << 17),      # 9,437,184 rows of 512 B: 4.83 GB
+    (128, 576, "fp8", 8, 1 << 20),     # 8,388,608 rows of 576 B: 4.83 GB
+    (32, 512, "bf16", 8, 5 << 17),     # 5,242,880 rows of 1 KiB: 5.37 GB (32-head kernel)
+]
+
+
+@pytest.mark.parametrize("H,D,kv,T,ctx", BIG_POOLS)
+def test_pool_larger_than_4gib(H, D, kv, T, ctx):
+    """Slot ids whose rows start past byte 2^32 of the pool gather those rows
+    (row r sits at byte r * row_bytes, formed without 32-bit wrap-around)."""
+    spec = synth.small_spec(T=T, H=H, Dqk=D, K=2048, ctx=ctx, kv_dtype=kv, mode="decode",
+                            seed=H + D, sm_scale=1.0 / math.sqrt(D))
+    row_bytes = D * (2 if kv == "bf16" else 1)
+    N = spec.N
+    assert N * row_bytes > 1 << 32
+    print(f"pool past 4 GiB: H{H} D{D} {kv} N={N} ({N * row_bytes / 2**30:.2f} GiB)", flush=True)
+    case = synth.make_case(spec, device=DEV)
+    idx = case.topk_idx.cpu().numpy().copy()
+    first_high = -(-(1 << 32) // row_bytes)            # first row that starts at or past 2^32
+    rng = np.random.default_rng(H + D)
+    # token 0: only rows past 2^32, including the very last one; token 1: the
+    # rows just below and just above the boundary
+    idx[0] = rng.choice(np.arange(first_high, N), size=idx.shape[1], replace=False)
+    idx[0, 5] = N - 1
+    idx[1, :8] = np.arange(first_high - 4, first_high + 4)
+    high = (idx >= first_high).sum()
+    assert high >= idx.shape[1], high
+    idx_d = torch.from_numpy(idx).to(DEV)
+    for splits in (0, 1):
+        out, lse = run(case, num_splits=splits, idx=idx_d)
+        ref_out, ref_lse = oracle_for_tokens(case, idx=idx_d)
+        compare(out, lse, ref_out, ref_lse, kv, f"pool {N * row_bytes / 2**30:.2f} GiB H{H} D{D} {kv} S{splits}")
+    # a single entry past 2^32 returns that row exactly
+    flat = case.kv_pool.reshape(N, D)
+    one = torch.full((1, 64), -1, dtype=torch.int32, device=DEV)
+    for r in (first_high, N - 1):
+        one[0, 3] = r
+        o1, _ = sparse_mla_fwd_ex(case.q[:1], case.kv_pool, one, case.sm_scale, case.kv_scale,
+                                  num_splits=1)
+        torch.cuda.synchronize()
+        row = flat[r, :512]
+        want = row.float() if kv == "bf16" else row.view(torch.float8_e4m3fn).float() * np.float32(case.kv_scale)
+        want = want.to(torch.bfloat16)
+        want = torch.where(want == 0, torch.zeros_like(want), want).expand(H, 512)
+        assert torch.equal(o1[0].view(torch.int16), want.contiguous().view(torch.int16)), r
+    del case, flat
     torch.cuda.empty_cache()
 
 
