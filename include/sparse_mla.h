@@ -179,6 +179,34 @@ smla_status_t sparse_mla_fwd_varlen(const void* q, int64_t T, int64_t H, int64_t
                                     void* workspace, size_t workspace_bytes,
                                     void* stream, const smla_options_t* opts);
 
+/*
+ * sparse_mla_fwd_noalloc -- sparse_mla_fwd_ex for callers that cannot allocate
+ * device memory: code under HIP graph capture that may not call hipMalloc,
+ * tight serving loops, harnesses that forbid allocation.  It takes no
+ * workspace: split partials go to a scratch array of SMLA_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each device it runs on (from the first call on that
+ * device until the process ends).  The call itself allocates nothing.
+ *
+ * Arguments, results and errors as sparse_mla_fwd_ex.  With options.num_splits
+ * = 0 the library's split choice is capped so that its partials
+ * (splits * T * H * 1044 bytes; none for one split) fit the scratch; an explicit
+ * num_splits whose partials do not fit returns SMLA_ERR_WORKSPACE before
+ * anything is launched.  Every call on a device shares that device's scratch:
+ * two calls that may overlap on one device (different streams without
+ * ordering between them) race and give undefined results; calls ordered on
+ * one stream are safe.  The scratch needs no clearing between calls (every
+ * partial is written before the merge reads it).
+ */
+#define SMLA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+smla_status_t sparse_mla_fwd_noalloc(const void* q, int64_t T, int64_t H, int64_t Dqk,
+                                     int64_t q_stride_t, int64_t q_stride_h,
+                                     const void* kv_pool, int32_t kv_dtype,
+                                     int64_t num_blocks, int64_t block_size,
+                                     const int32_t* topk_idx, int64_t K, int64_t idx_stride_t,
+                                     float sm_scale, float kv_scale,
+                                     void* out, float* lse,
+                                     void* stream, const smla_options_t* opts);
+
 /* Workspace bytes sparse_mla_fwd_varlen needs (queries the current device's
  * CU count).  Returns (size_t)-1 on error. */
 size_t sparse_mla_workspace_bytes_varlen(int64_t T, int64_t H, int64_t K, int64_t Dqk,

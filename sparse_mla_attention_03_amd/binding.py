@@ -23,6 +23,7 @@ MAX_SPLITS = 64
 DOTS_DEFAULT = 0
 DOTS_BF16 = 1
 ABI_VERSION = 3
+NOALLOC_SCRATCH_BYTES = 32 << 20   # SMLA_NOALLOC_SCRATCH_BYTES
 
 STATUS_NAMES = {0: "SMLA_OK", 1: "SMLA_ERR_NULL", 2: "SMLA_ERR_SHAPE", 3: "SMLA_ERR_DTYPE",
                 4: "SMLA_ERR_ALIGN", 5: "SMLA_ERR_INVALID_ARG", 6: "SMLA_ERR_UNSUPPORTED",
@@ -62,6 +63,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sparse_mla_fwd.restype = ctypes.c_int
     lib.sparse_mla_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(Options)]
     lib.sparse_mla_fwd_ex.restype = ctypes.c_int
+    lib.sparse_mla_fwd_noalloc.argtypes = fwd_args[:17] + [vp, ctypes.POINTER(Options)]
+    lib.sparse_mla_fwd_noalloc.restype = ctypes.c_int
     lib.sparse_mla_num_splits.argtypes = [i64, i64, i64, i64, i32, i32]
     lib.sparse_mla_num_splits.restype = i32
     lib.sparse_mla_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
@@ -143,21 +146,8 @@ def _pool_shape(kv_pool: torch.Tensor):
     return nb, bs, D
 
 
-def sparse_mla_fwd_ex(q: torch.Tensor, kv_pool: torch.Tensor, topk_idx: torch.Tensor,
-                      sm_scale: float, kv_scale: float = 1.0, out: torch.Tensor | None = None,
-                      lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                      num_splits: int = 0, stream=None, kernel_events=None,
-                      sinks: torch.Tensor | None = None, dot_precision: int = 0,
-                      q_scale: float = 0.0):
-    """Sparse MLA forward; returns (out bf16 [T,H,512], lse fp32 [T,H]).
-
-    kernel_events: optional pair of raw hipEvent_t handles (ints) the library
-    records around its main kernel (instrumentation for benchmarks).
-    sinks: optional float32 [H] per-head sink logits on q's device.
-    dot_precision: DOTS_DEFAULT or DOTS_BF16 (e4m3 KV only).
-    q_scale: > 0 when q is already quantised: q then holds OCP e4m3 codes (uint8 or
-    float8_e4m3fn) and qhat = q_scale * code (e4m3 KV with e4m3 dots only)."""
-    lib = load_library()
+def _fwd_operands(q, kv_pool, topk_idx, out, lse, q_scale):
+    """Checks shared by the forward entry points; returns the sizes and out / lse."""
     if q_scale > 0:
         if q.dim() != 3 or q.dtype not in (torch.uint8, torch.float8_e4m3fn):
             raise TypeError("pre-quantised q must be uint8 / float8_e4m3fn [T, H, Dqk]")
@@ -190,14 +180,10 @@ def sparse_mla_fwd_ex(q: torch.Tensor, kv_pool: torch.Tensor, topk_idx: torch.Te
         raise ValueError("out must be a contiguous bfloat16 [T, H, 512] tensor")
     if lse.shape != (T, H) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [T, H] tensor")
-    ws_ptr, ws_bytes = None, 0
-    if T > 0:
-        need = sparse_mla_workspace_bytes(T, H, K, D, kvd, num_splits)
-        if need > 0:
-            if workspace is None or workspace.numel() * workspace.element_size() < need:
-                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-            ws_ptr = workspace.data_ptr()
-            ws_bytes = workspace.numel() * workspace.element_size()
+    return T, H, D, nb, bs, kvd, K, out, lse
+
+
+def _fwd_options(H, q, num_splits, dot_precision, q_scale, sinks, kernel_events=None):
     opts = Options()
     opts.num_splits = num_splits
     opts.dot_precision = dot_precision
@@ -210,12 +196,61 @@ def sparse_mla_fwd_ex(q: torch.Tensor, kv_pool: torch.Tensor, topk_idx: torch.Te
         opts.sinks = sinks.data_ptr()
     if kernel_events is not None:
         opts.kernel_events[0], opts.kernel_events[1] = kernel_events
+    return opts
+
+
+def sparse_mla_fwd_ex(q: torch.Tensor, kv_pool: torch.Tensor, topk_idx: torch.Tensor,
+                      sm_scale: float, kv_scale: float = 1.0, out: torch.Tensor | None = None,
+                      lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      num_splits: int = 0, stream=None, kernel_events=None,
+                      sinks: torch.Tensor | None = None, dot_precision: int = 0,
+                      q_scale: float = 0.0):
+    """Sparse MLA forward; returns (out bf16 [T,H,512], lse fp32 [T,H]).
+
+    kernel_events: optional pair of raw hipEvent_t handles (ints) the library
+    records around its main kernel (instrumentation for benchmarks).
+    sinks: optional float32 [H] per-head sink logits on q's device.
+    dot_precision: DOTS_DEFAULT or DOTS_BF16 (e4m3 KV only).
+    q_scale: > 0 when q is already quantised: q then holds OCP e4m3 codes (uint8 or
+    float8_e4m3fn) and qhat = q_scale * code (e4m3 KV with e4m3 dots only)."""
+    lib = load_library()
+    T, H, D, nb, bs, kvd, K, out, lse = _fwd_operands(q, kv_pool, topk_idx, out, lse, q_scale)
+    ws_ptr, ws_bytes = None, 0
+    if T > 0:
+        need = sparse_mla_workspace_bytes(T, H, K, D, kvd, num_splits)
+        if need > 0:
+            if workspace is None or workspace.numel() * workspace.element_size() < need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            ws_ptr = workspace.data_ptr()
+            ws_bytes = workspace.numel() * workspace.element_size()
+    opts = _fwd_options(H, q, num_splits, dot_precision, q_scale, sinks, kernel_events)
     st = lib.sparse_mla_fwd_ex(
         q.data_ptr(), T, H, D, q.stride(0) if T else 0, q.stride(1) if T else 0,
         kv_pool.data_ptr(), kvd, nb, bs,
         topk_idx.data_ptr() if topk_idx.numel() else None, K, topk_idx.stride(0) if T else 0,
         float(sm_scale), float(kv_scale), out.data_ptr(), lse.data_ptr(),
         ws_ptr, ws_bytes, _stream_handle(q.device, stream), ctypes.byref(opts))
+    _check(st)
+    return out, lse
+
+
+def sparse_mla_fwd_noalloc(q: torch.Tensor, kv_pool: torch.Tensor, topk_idx: torch.Tensor,
+                           sm_scale: float, kv_scale: float = 1.0, out: torch.Tensor | None = None,
+                           lse: torch.Tensor | None = None, num_splits: int = 0, stream=None,
+                           sinks: torch.Tensor | None = None, dot_precision: int = 0,
+                           q_scale: float = 0.0):
+    """sparse_mla_fwd_ex without a workspace: the library keeps the split partials in
+    its own per-device scratch array and allocates nothing during the call (pass
+    out / lse to keep this wrapper from allocating them)."""
+    lib = load_library()
+    T, H, D, nb, bs, kvd, K, out, lse = _fwd_operands(q, kv_pool, topk_idx, out, lse, q_scale)
+    opts = _fwd_options(H, q, num_splits, dot_precision, q_scale, sinks)
+    st = lib.sparse_mla_fwd_noalloc(
+        q.data_ptr(), T, H, D, q.stride(0) if T else 0, q.stride(1) if T else 0,
+        kv_pool.data_ptr(), kvd, nb, bs,
+        topk_idx.data_ptr() if topk_idx.numel() else None, K, topk_idx.stride(0) if T else 0,
+        float(sm_scale), float(kv_scale), out.data_ptr(), lse.data_ptr(),
+        _stream_handle(q.device, stream), ctypes.byref(opts))
     _check(st)
     return out, lse
 

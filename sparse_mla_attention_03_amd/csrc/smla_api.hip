@@ -58,6 +58,33 @@ smla_status_t device_cu_count(int* cus) {
   return SMLA_OK;
 }
 
+// ---- the allocation-free entry point's scratch ---------------------------------
+// Split partials of sparse_mla_fwd_noalloc live in this array instead of a caller
+// workspace.  Each device the library runs on holds its own copy until the
+// process ends.  Host code never uses the array's name as an address (on the host
+// it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = SMLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+smla_status_t device_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SMLA_ERR_UNSUPPORTED, "device %d beyond the %d devices the scratch table covers", dev, kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(SMLA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev].store(p, std::memory_order_release);   // racing first calls store the same address
+  }
+  *ptr = p;
+  return SMLA_OK;
+}
+
 struct Plan {
   int32_t S = 1;        // split-K factor
   int32_t rps = 0;      // top-k entries per split (multiple of kBK)
@@ -147,7 +174,7 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
                        int64_t block_size, const int32_t* topk_idx, int64_t K, int64_t idx_stride_t,
                        float sm_scale, float kv_scale, void* out, float* lse, void* workspace,
                        size_t workspace_bytes, void* stream, const smla_options_t* opts,
-                       const int32_t* topk_len = nullptr) {
+                       const int32_t* topk_len = nullptr, bool noalloc = false) {
   g_last_error.clear();
   smla_status_t st = check_sizes(T, H, K, Dqk, kv_dtype);
   if (st != SMLA_OK) return st;
@@ -211,8 +238,22 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
     plan.ws_bytes = VL.total;
   } else {
     st = make_plan(T, H, K, req, &plan);
+    if (st == SMLA_OK && noalloc && plan.ws_bytes > kScratchBytes) {
+      // the library's own split choice is capped so its partials fit the scratch
+      // (one split needs none); an explicit request that does not fit is refused
+      if (req != 0)
+        return fail(SMLA_ERR_WORKSPACE, "%d splits need %zu bytes of partials, beyond the %zu-byte scratch",
+                    plan.S, plan.ws_bytes, kScratchBytes);
+      const int64_t fit = (int64_t)(kScratchBytes / ((size_t)T * H * kPartRowBytes));
+      st = make_plan(T, H, K, (int32_t)(fit > 1 ? fit : 1), &plan);
+    }
   }
   if (st != SMLA_OK) return st;
+  if (noalloc && plan.ws_bytes > 0) {
+    st = device_scratch(&workspace);
+    if (st != SMLA_OK) return st;
+    workspace_bytes = kScratchBytes;
+  }
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes)
       return fail(SMLA_ERR_WORKSPACE, "workspace of %zu bytes needed for %d splits, got %zu",
@@ -339,6 +380,17 @@ smla_status_t sparse_mla_fwd_ex(const void* q, int64_t T, int64_t H, int64_t Dqk
   return fwd_impl(q, T, H, Dqk, q_stride_t, q_stride_h, kv_pool, kv_dtype, num_blocks, block_size,
                   topk_idx, K, idx_stride_t, sm_scale, kv_scale, out, lse, workspace,
                   workspace_bytes, stream, opts);
+}
+
+smla_status_t sparse_mla_fwd_noalloc(const void* q, int64_t T, int64_t H, int64_t Dqk,
+                                     int64_t q_stride_t, int64_t q_stride_h, const void* kv_pool,
+                                     int32_t kv_dtype, int64_t num_blocks, int64_t block_size,
+                                     const int32_t* topk_idx, int64_t K, int64_t idx_stride_t,
+                                     float sm_scale, float kv_scale, void* out, float* lse,
+                                     void* stream, const smla_options_t* opts) {
+  return fwd_impl(q, T, H, Dqk, q_stride_t, q_stride_h, kv_pool, kv_dtype, num_blocks, block_size,
+                  topk_idx, K, idx_stride_t, sm_scale, kv_scale, out, lse, nullptr, 0, stream, opts,
+                  nullptr, true);
 }
 
 int32_t sparse_mla_num_splits(int64_t T, int64_t H, int64_t K, int64_t Dqk, int32_t kv_dtype,

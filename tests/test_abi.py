@@ -174,3 +174,25 @@ def test_varlen_validation(lib):
     st, msg = v(lens=P + 2)
     assert st == ALIGN and "topk_len" in msg
     assert v(T=0, q=None, kv=None, idx=None, out=None, lse=None, lens=None)[0] == OK
+
+
+def test_noalloc_rejects_explicit_splits_beyond_its_scratch(lib):
+    """An explicit split count whose partials exceed the per-device scratch is
+    refused on the host (SMLA_ERR_WORKSPACE) before any HIP call; a bad option
+    is refused as in sparse_mla_fwd_ex."""
+    opts = binding.Options()
+    T, H = 64, 128
+    splits = 8                                   # 8 * 64 * 128 * 1044 B > 32 MiB
+    assert splits * T * H * 1044 > 32 << 20
+    opts.num_splits = splits
+    st = lib.sparse_mla_fwd_noalloc(P, T, H, 576, H * 576, 576, P, 0, 512, 64, P, 2048, 2048,
+                                    0.04, 1.0, P, P, None, ctypes.byref(opts))
+    assert st == WS
+    assert "scratch" in binding.sparse_mla_last_error()
+    opts.num_splits = 99
+    st = lib.sparse_mla_fwd_noalloc(P, T, H, 576, H * 576, 576, P, 0, 512, 64, P, 2048, 2048,
+                                    0.04, 1.0, P, P, None, ctypes.byref(opts))
+    assert st == INVALID
+    # T == 0 is a no-op with null pointers, as for the other entry points
+    assert lib.sparse_mla_fwd_noalloc(None, 0, 16, 512, 0, 0, None, 0, 1, 64, None, 8, 8,
+                                      0.04, 1.0, None, None, None, None) == OK
