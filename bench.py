@@ -17,7 +17,14 @@ rate (every replay's time is in `batch_ms`).
 Prints ONE JSON line: value = gathered KV bytes / second (whole job), plus
 `roofline` for the main kernel (algorithmic gathered bytes / its own average
 duration, timed with HIP events the library records around it on the same
-stream) and `cpu_baseline` (the fp64 oracle on the host, same workload).
+stream; `frac_call` the same bytes over the whole call; `frac_measured` and
+`frac_call_measured` against the gather-only ceiling of the same index stream)
+and `cpu_baseline` (the fp64 oracle on the host, same workload).  The default
+run also measures the device ceilings (`ceilings`: streaming read, gather-only
+on each workload's own index stream, bf16 / e4m3 MFMA loops, from
+libsmla_ceiling.so) and times the other workloads the same way (`workloads`:
+e4m3 decode, the largest prefill shape, 576-wide rows with 128 heads in bf16 and
+e4m3), each with its own roofline fractions.
 """
 from __future__ import annotations
 
@@ -58,6 +65,13 @@ def parse():
                          "(FETCH_SIZE / WRITE_SIZE of this workload, then of --copy-calibration "
                          "--copy-bytes) into profiles/traffic_<workload>.json")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the device-ceiling probes (stream read, gather-only, MFMA loops)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the device ceilings (streaming read, MFMA loops, gather-only on "
+                         "every decode workload's index stream) and print them")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="time only --workload (the default run also times the other workloads)")
     ap.add_argument("--sensitivity", action="store_true",
                     help="also time (not part of value): each call after a 1 GiB read that "
                          "evicts the caches (cold; for prefill this is the cold first call), "
@@ -96,7 +110,7 @@ class HipEvents:
 
 # the sources of the forward pass's kernels and their launch configuration; the
 # fused RoPE / cache write is a kernel of its own and does not enter the hash
-FWD_SOURCES = ("smla_api.hip", "smla_device.h", "smla_kernels.h", "smla_kernels.hip")
+FWD_SOURCES = ("smla_api.hip", "smla_common.h", "smla_device.h", "smla_kernels.h", "smla_kernels.hip")
 
 
 def kernel_source_hash() -> str:
@@ -471,6 +485,242 @@ def mixed_bench(args) -> None:
         "batch_ms": [round(b, 4) for b in batch_ms]}), flush=True)
 
 
+# Workloads timed beside the headline one in the default run (every config of the
+# benchmark table that fits one GPU; the prefill shape is the largest of the twelve)
+SIDE_WORKLOADS = ("decode_fp8", "prefill_bf16_T2048_K2048", "rope_decode_bf16", "rope_decode_fp8")
+
+
+class Ceilings:
+    """The device's measured ceilings (libsmla_ceiling.so): streaming read, a
+    gather of each workload's own index stream with no arithmetic, MFMA loops."""
+
+    def __init__(self):
+        import torch
+        lib_path = os.path.join(ROOT, "sparse_mla_attention_03_amd", "csrc", "libsmla_ceiling.so")
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"{lib_path} is not built (run __graft_entry__.build())")
+        self.lib = ctypes.CDLL(lib_path)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        self.lib.smla_ceiling_stream_read.argtypes = [vp, i64, vp, i64, vp]
+        self.lib.smla_ceiling_gather.argtypes = [vp, i64, i32, vp, i64, i32, i32, vp, i64, vp]
+        self.lib.smla_ceiling_mfma.argtypes = [i32, i32, i32, vp, i64, vp]
+        self.sink = torch.empty(64 << 20, dtype=torch.uint8, device="cuda:0")
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def _time_ms(self, launch, reps: int) -> float:
+        """Time per launch: `reps` launches captured as one HIP graph, median of
+        BATCHES replays (as the workloads are timed: an isolated launch starts its
+        workgroups on the eight XCDs microseconds apart, a replayed one does not)."""
+        import numpy as np
+        import torch
+        launch(0)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.stream = side.cuda_stream
+            launch(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            self.stream = torch.cuda.current_stream().cuda_stream
+            for i in range(reps):
+                launch(i)
+        self.stream = torch.cuda.current_stream().cuda_stream
+        graph.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(BATCHES):
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0.record()
+            graph.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            ts.append(t0.elapsed_time(t1) / reps)
+        del graph
+        return float(np.median(ts))
+
+    def stream_read_gbs(self, nbytes: int = 2 << 30) -> float:
+        import torch
+        buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        def launch(_):
+            assert self.lib.smla_ceiling_stream_read(buf.data_ptr(), nbytes, self.sink.data_ptr(),
+                                                     self.sink.numel(), self.stream) == 0
+        ms = self._time_ms(launch, 10)
+        del buf
+        torch.cuda.empty_cache()
+        return nbytes / (ms * 1e-3) / 1e9
+
+    PATTERNS = ("row, 8 in flight", "row, 16 in flight", "8 rows x 128 B, 8 in flight",
+                "8 rows x 128 B, 16 in flight")
+
+    def gather_gbs(self, cases, row_bytes: int) -> dict:
+        """Best rate over access patterns and wave counts, rotating the workload's
+        index sets; every combination is in `all`."""
+        pool = cases[0].kv_pool
+        N = pool.shape[0] * pool.shape[1]
+        valid = sum(int(((c.topk_idx >= 0) & (c.topk_idx < N)).sum().item()) for c in cases) / len(cases)
+        best, every = None, {}
+        for pattern in range(4):
+            for waves in (1024, 2048, 4096):
+                def launch(i):
+                    idx = cases[i % len(cases)].topk_idx
+                    assert self.lib.smla_ceiling_gather(pool.data_ptr(), N, row_bytes, idx.data_ptr(), idx.numel(),
+                                                        waves, pattern, self.sink.data_ptr(), self.sink.numel(),
+                                                        self.stream) == 0
+                ms = self._time_ms(launch, 2 * len(cases))
+                gbs = valid * row_bytes / (ms * 1e-3) / 1e9
+                every[f"{self.PATTERNS[pattern]}, {waves} waves"] = round(gbs, 1)
+                if best is None or gbs > best["GB/s"]:
+                    best = {"GB/s": round(gbs, 1), "us": round(ms * 1e3, 3), "waves": waves,
+                            "pattern": self.PATTERNS[pattern]}
+        best["all"] = every
+        return best
+
+    def mfma_tflops(self, fp8: bool) -> float:
+        blocks, iters = 256 * 8, 2000
+        def launch(_):
+            assert self.lib.smla_ceiling_mfma(int(fp8), blocks, iters, self.sink.data_ptr(), self.sink.numel(),
+                                              self.stream) == 0
+        ms = self._time_ms(launch, 5)
+        flop = blocks * 4 * iters * 8 * (65536 if fp8 else 16384)
+        return flop / (ms * 1e-3) / 1e12
+
+
+def measure_workload(name: str, steps: int, warmup: int, ceilings=None, keep_cases: bool = False) -> dict:
+    """Time one workload: whole calls (graph replays) and the main kernel alone
+    (HIP events the library records around its own dispatch)."""
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_03_amd import synth
+    from sparse_mla_attention_03_amd.binding import (sparse_mla_fwd_ex, sparse_mla_num_splits,
+                                                     sparse_mla_workspace_bytes)
+
+    dev = torch.device("cuda:0")
+    spec = synth.CONFIGS[name]
+    cases = synth.make_case(spec, device="cuda:0", index_sets=INDEX_SETS)
+    kvd = 0 if spec.kv_dtype == "bf16" else 1
+    elem = 2 if spec.kv_dtype == "bf16" else 1
+    S = sparse_mla_num_splits(spec.T, spec.H, spec.K, spec.Dqk, kvd, 0)
+    ws_bytes = sparse_mla_workspace_bytes(spec.T, spec.H, spec.K, spec.Dqk, kvd, 0)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((spec.T, spec.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((spec.T, spec.H), dtype=torch.float32, device=dev)
+    valid_rows = [int(((c.topk_idx >= 0) & (c.topk_idx < spec.N)).sum().item()) for c in cases]
+    gathered = [v * spec.Dqk * elem for v in valid_rows]            # algorithmic bytes per call
+    flops = [v * 2 * spec.H * (spec.Dqk + 512) for v in valid_rows]  # algorithmic FLOP per call
+
+    def call(i, events=None):
+        c = cases[i % INDEX_SETS]
+        sparse_mla_fwd_ex(c.q, c.kv_pool, c.topk_idx, c.sm_scale, c.kv_scale, out=out, lse=lse,
+                          workspace=ws, num_splits=0, kernel_events=events)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    # ---- whole-job timing: the K calls captured once as a HIP graph (no host
+    # launch overhead inside the timed region), replayed back to back
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            call(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    # a replay must reproduce the eager result of its last call bit for bit
+    g_out, g_lse = out.clone(), lse.clone()
+    call(steps - 1)
+    torch.cuda.synchronize()
+    if not (torch.equal(g_out.view(torch.int16), out.view(torch.int16)) and torch.equal(g_lse, lse)):
+        raise RuntimeError(f"{name}: graph replay differs from the eager call")
+    # BATCHES replays of the K calls, each bracketed by synchronisations; the
+    # median batch is reported (all of them go into the line)
+    batch_ms = []
+    wall = 0.0
+    for _ in range(BATCHES):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record()
+        graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - wall0
+        batch_ms.append(t0.elapsed_time(t1))
+    del graph
+    ms_total = float(np.median(batch_ms))
+    ms_per_step = ms_total / steps
+    bytes_total = sum(gathered[i % INDEX_SETS] for i in range(steps))
+    flop_total = sum(flops[i % INDEX_SETS] for i in range(steps))
+    avg_bytes, avg_flop = bytes_total / steps, flop_total / steps
+    decode = spec.mode != "prefill"
+
+    # ---- main-kernel timing: HIP events the library records around that kernel
+    ev = HipEvents(steps)
+    for i in range(steps):
+        call(i, events=ev.pair(i))
+    torch.cuda.synchronize()
+    kern_ms = [ev.elapsed_ms(i) for i in range(steps)]
+    ev.close()
+    kern_avg_ms = float(np.mean(kern_ms))
+    gbs_kernel = avg_bytes / (kern_avg_ms * 1e-3) / 1e9
+    gbs_call = avg_bytes / (ms_per_step * 1e-3) / 1e9
+    tf_kernel = avg_flop / (kern_avg_ms * 1e-3) / 1e12
+    tf_call = avg_flop / (ms_per_step * 1e-3) / 1e12
+    mfma_peak = BF16_PEAK_TFLOPS
+    res = {"workload": name, "spec": spec, "splits": S, "us_per_call": round(ms_per_step * 1e3, 3),
+           "main_kernel_us": round(kern_avg_ms * 1e3, 3), "gathered_bytes_per_call": int(avg_bytes),
+           "flop_per_call": int(avg_flop), "gbs_call": round(gbs_call, 1), "gbs_kernel": round(gbs_kernel, 1),
+           "tflops_call": round(tf_call, 2), "tflops_kernel": round(tf_kernel, 2),
+           "batch_ms": [round(b, 4) for b in batch_ms], "wall_s": round(wall, 3)}
+    if decode:
+        res["value"], res["unit"] = round(bytes_total / (ms_total * 1e-3) / 1e9, 3), "GB/s"
+        res["roofline"] = {"bound": "hbm", "achieved": round(gbs_kernel, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(gbs_kernel / HBM_PEAK_GBS, 4),
+                           "frac_call": round(gbs_call / HBM_PEAK_GBS, 4),
+                           "traffic": traffic_from_profiles(name, avg_bytes)}
+        if ceilings is not None:
+            g = ceilings.gather_gbs(cases, spec.Dqk * elem)
+            res["gather_ceiling"] = g
+            res["roofline"]["measured_peak"] = g["GB/s"]
+            res["roofline"]["frac_measured"] = round(gbs_kernel / g["GB/s"], 4)
+            res["roofline"]["frac_call_measured"] = round(gbs_call / g["GB/s"], 4)
+    else:
+        res["value"], res["unit"] = round(flop_total / (ms_total * 1e-3) / 1e12, 3), "TFLOP/s"
+        res["roofline"] = {"bound": "mfma", "achieved": round(tf_kernel, 2), "peak": mfma_peak,
+                           "unit": "TFLOP/s", "frac": round(tf_kernel / mfma_peak, 4),
+                           "frac_call": round(tf_call / mfma_peak, 4),
+                           "traffic": traffic_from_profiles(name, avg_bytes)}
+        if ceilings is not None and getattr(ceilings, "mfma_bf16", None):
+            res["roofline"]["measured_peak"] = round(ceilings.mfma_bf16, 1)
+            res["roofline"]["frac_measured"] = round(tf_kernel / ceilings.mfma_bf16, 4)
+    if spec.kv_dtype == "fp8" and spec.H >= 64:
+        # at the ridge: the matrix side as well (e4m3 QK + bf16 PV)
+        res["mfma_tflops_kernel"] = round(tf_kernel, 2)
+    if keep_cases:
+        res["_cases"] = cases
+    else:
+        del cases
+        torch.cuda.empty_cache()
+    return res
+
+
+def _side_summary(r: dict) -> dict:
+    keep = ("splits", "us_per_call", "main_kernel_us", "value", "unit", "gbs_call", "gbs_kernel",
+            "tflops_call", "tflops_kernel", "roofline", "gather_ceiling", "batch_ms")
+    return {k: r[k] for k in keep if k in r}
+
+
 def main():
     args = parse()
     if args.traffic_summary:
@@ -492,109 +742,38 @@ def main():
         mixed_bench(args)
         return
 
-    import numpy as np
     import torch
 
-    from sparse_mla_attention_03_amd import synth
-    from sparse_mla_attention_03_amd.binding import (load_library, sparse_mla_fwd_ex,
-                                                     sparse_mla_num_splits,
-                                                     sparse_mla_workspace_bytes)
+    from sparse_mla_attention_03_amd.binding import load_library, sparse_mla_fwd_ex
 
     load_library()
-    dev = torch.device("cuda:0")
-    spec = synth.CONFIGS[args.workload]
-    cases = synth.make_case(spec, device="cuda:0", index_sets=INDEX_SETS)
-    kvd = 0 if spec.kv_dtype == "bf16" else 1
-    elem = 2 if spec.kv_dtype == "bf16" else 1
-    S = sparse_mla_num_splits(spec.T, spec.H, spec.K, spec.Dqk, kvd, 0)
-    ws_bytes = sparse_mla_workspace_bytes(spec.T, spec.H, spec.K, spec.Dqk, kvd, 0)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    out = torch.empty((spec.T, spec.H, 512), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((spec.T, spec.H), dtype=torch.float32, device=dev)
+    ceil = None
+    ceilings_line = None
+    if not args.no_ceilings:
+        ceil = Ceilings()
+        ceil.mfma_bf16 = ceil.mfma_tflops(False)
+        ceilings_line = {"stream_read_GBs": round(ceil.stream_read_gbs(), 1),
+                         "mfma_bf16_TFLOPs": round(ceil.mfma_bf16, 1),
+                         "mfma_fp8_TFLOPs": round(ceil.mfma_tflops(True), 1),
+                         "gather_GBs": {}}
+    if args.ceilings:
+        from sparse_mla_attention_03_amd import synth
+        for w in ("decode_bf16",) + SIDE_WORKLOADS:
+            spec = synth.CONFIGS[w]
+            if spec.mode == "prefill":
+                continue
+            cases = synth.make_case(spec, device="cuda:0", index_sets=INDEX_SETS)
+            ceilings_line["gather_GBs"][w] = ceil.gather_gbs(cases, spec.Dqk * (2 if spec.kv_dtype == "bf16" else 1))
+            del cases
+            torch.cuda.empty_cache()
+        print(json.dumps({"ceilings": ceilings_line}), flush=True)
+        return
 
-    valid_rows = []
-    for c in cases:
-        idx = c.topk_idx
-        valid_rows.append(int(((idx >= 0) & (idx < spec.N)).sum().item()))
-    gathered = [v * spec.Dqk * elem for v in valid_rows]            # algorithmic bytes per call
-    flops = [v * 2 * spec.H * (spec.Dqk + 512) for v in valid_rows]  # algorithmic FLOP per call
-
-    def call(i, events=None):
-        c = cases[i % INDEX_SETS]
-        sparse_mla_fwd_ex(c.q, c.kv_pool, c.topk_idx, c.sm_scale, c.kv_scale, out=out, lse=lse,
-                          workspace=ws, num_splits=0, kernel_events=events)
-
-    for i in range(args.warmup):
-        call(i)
-    torch.cuda.synchronize()
-
-    # ---- whole-job timing: the K calls captured once as a HIP graph (no host
-    # launch overhead inside the timed region), replayed back to back
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        call(0)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
-        for i in range(args.steps):
-            call(i)
-    graph.replay()
-    torch.cuda.synchronize()
-    # a replay must reproduce the eager result of its last call bit for bit
-    g_out, g_lse = out.clone(), lse.clone()
-    call(args.steps - 1)
-    torch.cuda.synchronize()
-    if not (torch.equal(g_out.view(torch.int16), out.view(torch.int16)) and torch.equal(g_lse, lse)):
-        raise RuntimeError("graph replay differs from the eager call")
-    # BATCHES replays of the K calls, each bracketed by synchronisations; the
-    # median batch is reported (all of them go into the line)
-    batch_ms = []
-    wall = 0.0
-    for _ in range(BATCHES):
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        t0.record()
-        graph.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        wall += time.perf_counter() - wall0
-        batch_ms.append(t0.elapsed_time(t1))
-    ms_total = float(np.median(batch_ms))
-    ms_per_step = ms_total / args.steps
-    bytes_total = sum(gathered[i % INDEX_SETS] for i in range(args.steps))
-    flop_total = sum(flops[i % INDEX_SETS] for i in range(args.steps))
-    decode = spec.mode != "prefill"
-    if decode:
-        value, unit = bytes_total / (ms_total * 1e-3) / 1e9, "GB/s"
-    else:
-        value, unit = flop_total / (ms_total * 1e-3) / 1e12, "TFLOP/s"
-    del graph
-
-    # ---- main-kernel timing: HIP events the library records around that kernel
-    ev = HipEvents(args.steps)
-    for i in range(args.steps):
-        call(i, events=ev.pair(i))
-    torch.cuda.synchronize()
-    kern_ms = [ev.elapsed_ms(i) for i in range(args.steps)]
-    ev.close()
-    kern_avg_ms = float(np.mean(kern_ms))
-    avg_bytes = bytes_total / args.steps
-    avg_flop = flop_total / args.steps
-    achieved = avg_bytes / (kern_avg_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(args.workload, avg_bytes)
-
-    if decode:
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
-    else:
-        tflops = avg_flop / (kern_avg_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                    "traffic": traffic}
+    main_res = measure_workload(args.workload, args.steps, args.warmup, ceil, keep_cases=True)
+    cases = main_res.pop("_cases")
+    spec = main_res["spec"]
+    if ceilings_line is not None and "gather_ceiling" in main_res:
+        ceilings_line["gather_GBs"][args.workload] = main_res["gather_ceiling"]
 
     cpu = cpu1 = None
     if not args.no_cpu_baseline:
@@ -602,20 +781,33 @@ def main():
         cpu1 = cpu_single_thread(staged)
     sens = None
     if args.sensitivity:
+        out = torch.empty((spec.T, spec.H, 512), dtype=torch.bfloat16, device="cuda:0")
+        lse = torch.empty((spec.T, spec.H), dtype=torch.float32, device="cuda:0")
+
         def call_case(c):
             sparse_mla_fwd_ex(c.q, c.kv_pool, c.topk_idx, c.sm_scale, c.kv_scale, out=out, lse=lse,
-                              workspace=ws, num_splits=0)
+                              num_splits=0)
         sens = sensitivity(spec, cases, call_case, args.steps)
+    del cases
+    torch.cuda.empty_cache()
+
+    side = {}
+    if not args.no_workloads and args.workload == "decode_bf16":
+        for w in SIDE_WORKLOADS:
+            r = measure_workload(w, args.steps, args.warmup, ceil)
+            side[w] = _side_summary(r)
+            if ceilings_line is not None and "gather_ceiling" in r:
+                ceilings_line["gather_GBs"][w] = r["gather_ceiling"]
 
     line = {
         "metric": "sparse-MLA decode \u00b5s/call + gathered-KV HBM GB/s; prefill TFLOP/s (1 MI355X)",
-        "value": round(value, 3),
-        "unit": unit,
+        "value": main_res["value"],
+        "unit": main_res["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
-        "us_per_call": round(ms_per_step * 1e3, 3),
+        "ms_per_step": round(main_res["us_per_call"] / 1e3, 6),
+        "us_per_call": main_res["us_per_call"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -623,16 +815,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": spec.name, "tokens": spec.T, "heads": spec.H, "dqk": spec.Dqk,
                    "dv": 512, "topk": spec.K, "context": spec.ctx, "block_size": spec.block_size,
-                   "kv": spec.kv_dtype, "splits": S, "index_sets": INDEX_SETS,
-                   "gathered_bytes_per_call": int(avg_bytes),
-                   "tflops": round(avg_flop / (ms_per_step * 1e-3) / 1e12, 3)},
-        "roofline": roofline,
-        "main_kernel_us": round(kern_avg_ms * 1e3, 3),
+                   "kv": spec.kv_dtype, "splits": main_res["splits"], "index_sets": INDEX_SETS,
+                   "gathered_bytes_per_call": main_res["gathered_bytes_per_call"],
+                   "tflops": main_res["tflops_call"]},
+        "roofline": main_res["roofline"],
+        "main_kernel_us": main_res["main_kernel_us"],
         "cpu_baseline": cpu,
         "cpu_baseline_1_thread": cpu1,
-        "batch_ms": [round(b, 4) for b in batch_ms],
-        "wall_s": round(wall, 3),
+        "batch_ms": main_res["batch_ms"],
+        "wall_s": main_res["wall_s"],
     }
+    if ceilings_line is not None:
+        line["ceilings"] = ceilings_line
+    if side:
+        line["workloads"] = side
     if sens is not None:
         line["sensitivity"] = sens
     print(json.dumps(line), flush=True)

@@ -3,7 +3,9 @@
     python -m sparse_mla_attention_03_amd.csrc.build      # or build.build()
 
 The translation units compile in parallel, then link into one shared
-library exporting the C ABI of include/sparse_mla.h.
+library exporting the C ABI of include/sparse_mla.h.  The device-ceiling
+probes the benchmark reports beside it (include/smla_ceiling.h) go into a
+library of their own, libsmla_ceiling.so.
 """
 from __future__ import annotations
 
@@ -17,6 +19,8 @@ ROOT = os.path.dirname(os.path.dirname(HERE))
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsparsemla.so")
 SOURCES = ["smla_api.hip", "smla_kernels.hip", "smla_rope_cache.hip"]
+CEILING_LIB = os.path.join(HERE, "libsmla_ceiling.so")
+CEILING_SOURCES = ["smla_ceiling.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -57,14 +61,15 @@ def build(verbose: bool = False) -> str:
             print(msgs)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(CEILING_SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + CEILING_SOURCES))
+    for lib, o in ((LIB, objs[:len(SOURCES)]), (CEILING_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp"
+        cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *o]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n{r.stdout}{r.stderr}")
+        os.replace(tmp, lib)
     return LIB
 
 

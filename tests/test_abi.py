@@ -196,3 +196,19 @@ def test_noalloc_rejects_explicit_splits_beyond_its_scratch(lib):
     # T == 0 is a no-op with null pointers, as for the other entry points
     assert lib.sparse_mla_fwd_noalloc(None, 0, 16, 512, 0, 0, None, 0, 1, 64, None, 8, 8,
                                       0.04, 1.0, None, None, None, None) == OK
+
+
+def test_ceiling_library_exports_its_header():
+    """The device-ceiling probes the benchmark loads (a library of their own)."""
+    text = open(os.path.join(ROOT, "include", "smla_ceiling.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(smla_ceiling_\w+)\s*\(", text)))
+    assert names == ["smla_ceiling_gather", "smla_ceiling_mfma", "smla_ceiling_stream_read"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_mla_attention_03_amd", "csrc", "libsmla_ceiling.so"))
+    for n in names:
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+    # argument checks return before any launch
+    lib.smla_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                             ctypes.c_int64, ctypes.c_void_p]
+    assert lib.smla_ceiling_stream_read(None, 1 << 20, None, 0, None) == 1
+    assert lib.smla_ceiling_stream_read(P, 1 << 20, P, 16, None) == 2
