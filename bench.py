@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="split count passed to the library (0 = its own choice; a sensitivity "
+                         "setting, not the workload)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -110,7 +113,8 @@ class HipEvents:
 
 # the sources of the forward pass's kernels and their launch configuration; the
 # fused RoPE / cache write is a kernel of its own and does not enter the hash
-FWD_SOURCES = ("smla_api.hip", "smla_common.h", "smla_device.h", "smla_kernels.h", "smla_kernels.hip")
+FWD_SOURCES = ("smla_api.hip", "smla_common.h", "smla_device.h", "smla_kernels.h", "smla_kernels.hip",
+               "smla_prefill.hip")
 
 
 def kernel_source_hash() -> str:
@@ -504,6 +508,7 @@ class Ceilings:
         self.lib.smla_ceiling_stream_read.argtypes = [vp, i64, vp, i64, vp]
         self.lib.smla_ceiling_gather.argtypes = [vp, i64, i32, vp, i64, i32, i32, vp, i64, vp]
         self.lib.smla_ceiling_mfma.argtypes = [i32, i32, i32, vp, i64, vp]
+        self.lib.smla_ceiling_lds_read.argtypes = [i32, i32, i32, vp, i64, vp]
         self.sink = torch.empty(64 << 20, dtype=torch.uint8, device="cuda:0")
         self.stream = torch.cuda.current_stream().cuda_stream
 
@@ -580,6 +585,18 @@ class Ceilings:
         best["all"] = every
         return best
 
+    def lds_read_bytes_per_clk(self, waves_per_cu: int, clk_ghz: float = 2.4) -> float:
+        """LDS read bandwidth per compute unit (bytes per clock at clk_ghz), one
+        workgroup of waves_per_cu waves on each of 256 compute units."""
+        blocks, iters = 256, 4000
+        threads = 64 * waves_per_cu
+        def launch(_):
+            assert self.lib.smla_ceiling_lds_read(blocks, threads, iters, self.sink.data_ptr(),
+                                                  self.sink.numel(), self.stream) == 0
+        ms = self._time_ms(launch, 5)
+        per_cu = threads * iters * 128 / (ms * 1e-3)
+        return per_cu / (clk_ghz * 1e9)
+
     def mfma_tflops(self, fp8: bool) -> float:
         blocks, iters = 256 * 8, 2000
         def launch(_):
@@ -590,7 +607,8 @@ class Ceilings:
         return flop / (ms * 1e-3) / 1e12
 
 
-def measure_workload(name: str, steps: int, warmup: int, ceilings=None, keep_cases: bool = False) -> dict:
+def measure_workload(name: str, steps: int, warmup: int, ceilings=None, keep_cases: bool = False,
+                     num_splits: int = 0) -> dict:
     """Time one workload: whole calls (graph replays) and the main kernel alone
     (HIP events the library records around its own dispatch)."""
     import numpy as np
@@ -605,8 +623,8 @@ def measure_workload(name: str, steps: int, warmup: int, ceilings=None, keep_cas
     cases = synth.make_case(spec, device="cuda:0", index_sets=INDEX_SETS)
     kvd = 0 if spec.kv_dtype == "bf16" else 1
     elem = 2 if spec.kv_dtype == "bf16" else 1
-    S = sparse_mla_num_splits(spec.T, spec.H, spec.K, spec.Dqk, kvd, 0)
-    ws_bytes = sparse_mla_workspace_bytes(spec.T, spec.H, spec.K, spec.Dqk, kvd, 0)
+    S = sparse_mla_num_splits(spec.T, spec.H, spec.K, spec.Dqk, kvd, num_splits)
+    ws_bytes = sparse_mla_workspace_bytes(spec.T, spec.H, spec.K, spec.Dqk, kvd, num_splits)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty((spec.T, spec.H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((spec.T, spec.H), dtype=torch.float32, device=dev)
@@ -617,7 +635,7 @@ def measure_workload(name: str, steps: int, warmup: int, ceilings=None, keep_cas
     def call(i, events=None):
         c = cases[i % INDEX_SETS]
         sparse_mla_fwd_ex(c.q, c.kv_pool, c.topk_idx, c.sm_scale, c.kv_scale, out=out, lse=lse,
-                          workspace=ws, num_splits=0, kernel_events=events)
+                          workspace=ws, num_splits=num_splits, kernel_events=events)
 
     for i in range(warmup):
         call(i)
@@ -755,6 +773,8 @@ def main():
         ceilings_line = {"stream_read_GBs": round(ceil.stream_read_gbs(), 1),
                          "mfma_bf16_TFLOPs": round(ceil.mfma_bf16, 1),
                          "mfma_fp8_TFLOPs": round(ceil.mfma_tflops(True), 1),
+                         "lds_read_B_per_clk_per_cu_at_2.4GHz": {
+                             f"{w} waves": round(ceil.lds_read_bytes_per_clk(w), 1) for w in (4, 8, 16)},
                          "gather_GBs": {}}
     if args.ceilings:
         from sparse_mla_attention_03_amd import synth
@@ -769,7 +789,8 @@ def main():
         print(json.dumps({"ceilings": ceilings_line}), flush=True)
         return
 
-    main_res = measure_workload(args.workload, args.steps, args.warmup, ceil, keep_cases=True)
+    main_res = measure_workload(args.workload, args.steps, args.warmup, ceil, keep_cases=True,
+                                num_splits=args.num_splits)
     cases = main_res.pop("_cases")
     spec = main_res["spec"]
     if ceilings_line is not None and "gather_ceiling" in main_res:

@@ -35,6 +35,14 @@ int smla_ceiling_stream_read(const void* src, int64_t bytes, void* sink, int64_t
 int smla_ceiling_gather(const void* kv_pool, int64_t N, int32_t row_bytes, const int32_t* idx, int64_t n_entries,
                         int32_t waves, int32_t pattern, void* sink, int64_t sink_bytes, void* stream);
 
+/* LDS read bandwidth: `blocks` workgroups of `threads` (64 .. 1024, a multiple
+ * of 64) threads, each wave `iters` rounds of 8 x 16-byte LDS reads per lane at
+ * conflict-free addresses of a 64 KiB buffer (one workgroup per compute unit).
+ * sink >= blocks * threads * 4 bytes.  Rate = blocks * threads * iters * 128
+ * bytes / kernel time. */
+int smla_ceiling_lds_read(int32_t blocks, int32_t threads, int32_t iters, void* sink, int64_t sink_bytes,
+                          void* stream);
+
 /* MFMA throughput: `blocks` workgroups of four waves, each wave `iters` rounds
  * of 8 independent v_mfma_f32_16x16x32_bf16 (fp8 = 0: 16384 FLOP each) or
  * v_mfma_scale_f32_16x16x128_f8f6f4 on e4m3 (fp8 != 0: 65536 FLOP each).

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsparsemla.so")
-SOURCES = ["smla_api.hip", "smla_kernels.hip", "smla_rope_cache.hip"]
+SOURCES = ["smla_api.hip", "smla_kernels.hip", "smla_prefill.hip", "smla_rope_cache.hip"]
 CEILING_LIB = os.path.join(HERE, "libsmla_ceiling.so")
 CEILING_SOURCES = ["smla_ceiling.hip"]
 ARCH = "gfx950"

@@ -299,10 +299,19 @@ smla_status_t fwd_impl(const void* q, int64_t T, int64_t H, int64_t Dqk, int64_t
     p.part_scale = reinterpret_cast<float*>(p.part_o + rows * smla::kDV);
     p.part_lse = p.part_scale + rows * 4;
   }
+  // whole long lists of 512-wide bf16 rows in 16-head groups, with at least
+  // two workgroups per compute unit: the kernel that runs two per unit
+  if (plan.S == 1 && !varlen && kv_dtype == SMLA_KV_BF16 && Dqk == 512 && smla::heads_per_workgroup(H) == 16 &&
+      K > 128) {
+    int cus = 0;
+    st = device_cu_count(&cus);
+    if (st != SMLA_OK) return st;
+    p.prefill16 = T * (H / 16) >= 2 * (int64_t)cus ? 1 : 0;
+  }
   if (getenv("SPARSEMLA_LOG"))
-    fprintf(stderr, "[sparsemla] T=%lld H=%lld Dqk=%lld K=%lld kv=%s splits=%d rows/split=%d\n",
+    fprintf(stderr, "[sparsemla] T=%lld H=%lld Dqk=%lld K=%lld kv=%s splits=%d rows/split=%d prefill16=%d\n",
             (long long)T, (long long)H, (long long)Dqk, (long long)K, kv_dtype ? "e4m3" : "bf16",
-            plan.S, plan.rps);
+            plan.S, plan.rps, p.prefill16);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (varlen) {

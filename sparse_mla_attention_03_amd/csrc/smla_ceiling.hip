@@ -8,6 +8,8 @@
 //                 loads in two access patterns (one row per 64-lane load, or
 //                 eight rows x 128 bytes per load), no arithmetic beyond
 //                 folding the bytes into one word per lane so the loads are live
+//   lds read      16-byte LDS reads at conflict-free addresses, 1 - 16 waves
+//                 per compute unit
 //   mfma          back-to-back v_mfma_f32_16x16x32_bf16 (or the e4m3
 //                 16x16x128 form) on independent accumulators
 #include <hip/hip_runtime.h>
@@ -91,6 +93,27 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const uint8_t* __restr
   sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = acc;
 }
 
+// LDS reads: each wave reads `iters` rounds of 8 x 16 bytes per lane from a
+// 64 KiB workgroup buffer at conflict-free addresses (lane l, read j: chunk
+// (l + 64 j + 512 wave) mod 4096), folding them into one word.
+__global__ __launch_bounds__(1024) void lds_read_kernel(int iters, uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[65536];
+  for (int i = threadIdx.x; i < 4096; i += blockDim.x)
+    *reinterpret_cast<u32x4*>(buf + 16 * i) = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t acc = 0;
+  for (int it = 0; it < iters; ++it) {
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = *reinterpret_cast<const u32x4*>(buf + 16 * ((lane + 64 * j + 512 * wave + it) & 4095));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= v[j][0] ^ v[j][3];
+  }
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 // MFMA: each wave runs `iters` rounds of 8 independent accumulator chains.
 template <bool FP8>
 __global__ __launch_bounds__(kThreads) void mfma_kernel(int iters, float* __restrict__ sink) {
@@ -166,6 +189,15 @@ int smla_ceiling_gather(const void* kv_pool, int64_t N, int32_t row_bytes, const
     default: return 1;
   }
 #undef SMLA_GATHER
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+int smla_ceiling_lds_read(int32_t blocks, int32_t threads, int32_t iters, void* sink, int64_t sink_bytes,
+                          void* stream) {
+  if (!sink || blocks < 1 || iters < 1 || threads < 64 || threads > 1024 || threads % 64) return 1;
+  if (sink_bytes < (int64_t)blocks * threads * 4) return 2;
+  hipLaunchKernelGGL(lds_read_kernel, dim3(blocks), dim3(threads), 0, static_cast<hipStream_t>(stream), iters,
+                     static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 

@@ -3,6 +3,8 @@
 // addresses, tile geometry and LDS access helpers.
 #pragma once
 
+#include <type_traits>
+
 #include "smla_device.h"
 #include "smla_kernels.h"
 
@@ -210,6 +212,76 @@ constexpr float kSlack = 8.0f;   // log2 headroom of the lazily rescaled running
 // 16 different chunk positions) and rows 2j, 2j + 1 differ in bit 3 of it, so
 // the two rows a 16-lane quarter of a commit store writes side by side fall in
 // different halves of the bank space.
-__device__ __forceinline__ int row_key(int r) { return ((r & 1) << 3) | ((r >> 1) & 7); }
+__host__ __device__ constexpr int row_key(int r) { return ((r & 1) << 3) | ((r >> 1) & 7); }
+
+// ---- scalar id loads, hand-counted LDS copies ---------------------------------------
+typedef __attribute__((ext_vector_type(4))) int32_t i32x4;
+typedef __attribute__((ext_vector_type(16))) int32_t i32x16;
+
+// s_buffer_load_dwordx8 / x16: scalar loads through a buffer descriptor
+// (dwords past num_records read 0); they use no vector memory counter.
+__device__ i32x8 sbuf_load_x8(i32x4 rsrc, int offset, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v8i32");
+__device__ i32x16 sbuf_load_x16(i32x4 rsrc, int offset, int cachepolicy) __asm("llvm.amdgcn.s.buffer.load.v16i32");
+
+// buffer descriptor over `bytes` bytes at p (wave-uniform)
+__device__ __forceinline__ i32x4 scalar_rsrc(const void* p, int bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = kBufferRsrcWord3;
+  return r;
+}
+
+// wait until at most N vector memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wait until this wave's LDS (and scalar memory) operations have completed
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// LDS byte address of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// global_load_lds_dwordx4: 64 lanes x 16 bytes from global memory into 1 KiB
+// of LDS at `lds` (wave-uniform; lane l's bytes land at lds + 16 l), with no
+// register result.  Written as asm: the compiler would otherwise wait for
+// every such copy (vmcnt(0)) before any LDS read it cannot prove disjoint,
+// which drains a pipeline of copies; kernels that use these wait for them
+// themselves (wait_vmcnt with the number of copies issued after the ones
+// needed).  M0 carries the LDS address (one wait state after writing it).
+// Kernels using them index no register array dynamically (M0 is theirs).
+// scalar row base + per-lane byte offset
+__device__ __forceinline__ void copy_s(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+// scalar row base + lane offset lane16 ^ KEY16 (lane16 = 16 * lane): the
+// offset is formed inside the copy, so no register holds it between copies
+template <uint32_t KEY16>
+__device__ __forceinline__ void copy_sx(const uint8_t* base, uint32_t lane16, uint32_t lds) {
+  uint32_t off;
+  asm volatile("v_xor_b32 %0, %1, %2\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %4"
+               : "=&v"(off)
+               : "i"(KEY16), "v"(lane16), "s"(lds), "s"(base)
+               : "memory", "m0");
+}
+// compile-time loop: f(std::integral_constant<int, I>) for I in [B, E)
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+// per-lane 64-bit address
+__device__ __forceinline__ void copy_v(const uint8_t* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
 
 }  // namespace smla

@@ -38,6 +38,8 @@ struct FwdParams {
   const int32_t* tok_count;     // [T] its unit count
   int32_t max_units;            // upper bound on U (the grid is sized for it)
   int32_t max_prows;            // partial rows in the workspace
+  int32_t prefill16;            // 1: 16-head groups of whole long bf16 lists, two
+                                // workgroups per compute unit (smla_prefill.hip)
 };
 
 // The fused q-RoPE / q-concat / KV-concat / cache write (strides in elements).
@@ -71,6 +73,8 @@ inline int heads_per_workgroup(int64_t H) { return (H % 64 == 0) ? 64 : (H % 32 
 hipError_t launch_fwd(const FwdParams& p, bool kv_fp8, bool bf16_dots, int dqk, hipStream_t stream,
                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_combine(const FwdParams& p, hipStream_t stream);
+// 16-head groups on whole long lists of 512-wide bf16 rows (smla_prefill.hip)
+hipError_t launch_prefill(const FwdParams& p, dim3 grid, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 // the per-token split plan from list lengths (one workgroup)
 struct PlanParams {
   const int32_t* lens;          // [T]

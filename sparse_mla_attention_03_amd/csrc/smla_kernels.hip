@@ -1832,6 +1832,9 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream, hipEvent_
       // q fragment read then feeds two 16-row blocks -- unless the list is so
       // short that each wave would get a single 32-row tile, with nothing to
       // overlap its gather (K <= 128: 16-row tiles measured 2 - 3 % faster).
+      if constexpr (!KV8 && DQK == 512) {
+        if (p.prefill16) return launch_prefill(p, gd, stream, ev0, ev1);
+      }
       if constexpr (KV8 || DQK == 512) {
         if (p.S > 1 || p.units != nullptr || p.K <= 4 * 32)
           hipExtLaunchKernelGGL((smla_rows_kernel<KV8, DQK, 16, QB>), gd, bd, 0, stream, ev0, ev1, 0, p);

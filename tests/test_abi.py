@@ -203,7 +203,7 @@ def test_ceiling_library_exports_its_header():
     text = open(os.path.join(ROOT, "include", "smla_ceiling.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(smla_ceiling_\w+)\s*\(", text)))
-    assert names == ["smla_ceiling_gather", "smla_ceiling_mfma", "smla_ceiling_stream_read"]
+    assert names == ["smla_ceiling_gather", "smla_ceiling_lds_read", "smla_ceiling_mfma", "smla_ceiling_stream_read"]
     lib = ctypes.CDLL(os.path.join(ROOT, "sparse_mla_attention_03_amd", "csrc", "libsmla_ceiling.so"))
     for n in names:
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value

@@ -71,6 +71,8 @@ MINIS = [
     (3, 192, 512, 100, 2048, "bf16", 64, 0.0),    # three 64-head groups
     (2, 64, 576, 40, 512, "bf16", 64, 0.3),       # shorter than one tile
     (2, 128, 512, 700, 8192, "fp8", 1, 0.1),      # many tiles, block size 1
+    (3, 48, 512, 333, 2048, "bf16", 64, 0.1),     # three 16-head groups, long lists
+    (2, 16, 512, 2047, 4096, "bf16", 1, 0.5),     # long list, half padding, ragged tail
 ]
 
 
@@ -350,6 +352,45 @@ def test_full_size_parity(name):
     compare(out, lse, ref_out, ref_lse, spec.kv_dtype, name)
     del case
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- whole long lists, two workgroups per CU
+
+# (head groups, K, ctx, pad_frac, sinks, strided q): enough (token, head group)
+# units for two workgroups per compute unit, so whole lists of 512-wide bf16
+# rows run on the kernel that holds two per unit
+PREFILL16 = [
+    (1, 300, 4096, 0.2, False, False),    # ragged last tile, padding anywhere
+    (1, 1100, 8192, 0.0, True, True),     # sinks, strided q
+    (3, 257, 2048, 0.1, True, False),     # three 16-head groups per token
+]
+
+
+@pytest.mark.parametrize("HG,K,ctx,pad,with_sinks,strided", PREFILL16)
+def test_whole_lists_two_workgroups_per_cu(HG, K, ctx, pad, with_sinks, strided):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    H = 16 * HG
+    T = (2 * cus + HG - 1) // HG + 5
+    case = gpu_case(T=T, H=H, Dqk=512, K=K, ctx=ctx, kv_dtype="bf16", block_size=64, seed=T + K)
+    assert binding.sparse_mla_num_splits(T, H, K, 512, 0, 0) == 1
+    idx = case.topk_idx.cpu().numpy().copy()
+    if pad > 0:
+        idx = synth.with_padding(idx, np.random.default_rng(K), pad)
+    N = case.spec.N
+    idx[0, 0], idx[1, 1], idx[2, 5], idx[3, :] = N, -2, 2**31 - 1, -1   # invalid spellings, an empty list
+    idx = torch.from_numpy(idx).to(DEV)
+    q = case.q
+    if strided:
+        big = torch.zeros((T, H, 512 + 64), dtype=torch.bfloat16, device=DEV)
+        big[:, :, :512] = case.q
+        q = big[:, :, :512]
+        assert q.stride(1) == 576
+    sinks = _gpu_sinks(H, K) if with_sinks else None
+    out, lse = sparse_mla_fwd_ex(q, case.kv_pool, idx, case.sm_scale, case.kv_scale,
+                                 sinks=None if sinks is None else torch.from_numpy(sinks).to(DEV))
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_for_tokens(case, idx=idx, sinks=sinks)
+    compare(out, lse, ref_out, ref_lse, "bf16", f"whole lists T{T} H{H} K{K}")
 
 
 # ---------------------------------------------------------------- pools past 4 GiB
