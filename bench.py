@@ -12,7 +12,10 @@ not fit the 256 MB Infinity Cache.
 
 The K steps are captured once as a HIP graph and replayed BATCHES times, each
 replay bracketed by synchronisations; the median replay gives the whole-job
-rate (every replay's time is in `batch_ms`).
+rate (every replay's time is in `batch_ms`).  Before the timed replays the
+graph is replayed untimed for about 0.1 s (besides the W warmup calls): the
+clocks need that long to settle (20-call replays of the 576-wide workload ran
+1.31 - 1.50 ms each right after set-up, ~1.15 ms once settled).
 
 Prints ONE JSON line: value = gathered KV bytes / second (whole job), plus
 `roofline` for the main kernel (algorithmic gathered bytes / its own average
@@ -196,6 +199,20 @@ def traffic_summary(workload: str, dirs, copy_bytes: int) -> None:
     print(json.dumps(rec), flush=True)
 
 
+WARM_S = 0.1   # untimed graph replays before timing: the clocks settle after ~100 ms of work
+
+
+def warm_replays(graph) -> None:
+    """Replay `graph` untimed for about WARM_S seconds (at least 3 times)."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while n < 3 or time.perf_counter() - t0 < WARM_S:
+        graph.replay()
+        torch.cuda.synchronize()
+        n += 1
+
+
 def graph_us_per_call(call, steps: int) -> float:
     """Median over BATCHES graph replays of `steps` captured calls, per call."""
     import numpy as np
@@ -213,8 +230,7 @@ def graph_us_per_call(call, steps: int) -> float:
     with torch.cuda.graph(graph):
         for i in range(steps):
             call(i)
-    graph.replay()
-    torch.cuda.synchronize()
+    warm_replays(graph)
     ms = []
     for _ in range(BATCHES):
         t0 = torch.cuda.Event(enable_timing=True)
@@ -374,8 +390,7 @@ def rope_cache_bench(args) -> None:
     with torch.cuda.graph(graph):
         for _ in range(args.steps):
             call()
-    graph.replay()
-    torch.cuda.synchronize()
+    warm_replays(graph)
     batch_ms = []
     for _ in range(BATCHES):
         t0 = torch.cuda.Event(enable_timing=True)
@@ -427,8 +442,7 @@ def _graph_us(fn, steps, warmup):
     with torch.cuda.graph(graph):
         for _ in range(steps):
             fn()
-    graph.replay()
-    torch.cuda.synchronize()
+    warm_replays(graph)
     ms = []
     for _ in range(BATCHES):
         t0 = torch.cuda.Event(enable_timing=True)
@@ -533,8 +547,7 @@ class Ceilings:
             for i in range(reps):
                 launch(i)
         self.stream = torch.cuda.current_stream().cuda_stream
-        graph.replay()
-        torch.cuda.synchronize()
+        warm_replays(graph)
         ts = []
         for _ in range(BATCHES):
             t0 = torch.cuda.Event(enable_timing=True)
@@ -660,6 +673,7 @@ def measure_workload(name: str, steps: int, warmup: int, ceilings=None, keep_cas
     torch.cuda.synchronize()
     if not (torch.equal(g_out.view(torch.int16), out.view(torch.int16)) and torch.equal(g_lse, lse)):
         raise RuntimeError(f"{name}: graph replay differs from the eager call")
+    warm_replays(graph)   # untimed: the clocks settle before the timed replays
     # BATCHES replays of the K calls, each bracketed by synchronisations; the
     # median batch is reported (all of them go into the line)
     batch_ms = []
