@@ -254,7 +254,9 @@ smla_status_t sparse_mla_quantize_q_fp8(const void* q, int64_t T, int64_t H, int
  * sin_i = cos_sin_cache[p, 32 + i] (i < 32):
  *   is_neox != 0: pairs (i, i + 32) ("rotate halves");  is_neox == 0: pairs (2i, 2i + 1)
  *   (x, y) -> (x cos_i - y sin_i, y cos_i + x sin_i)
- * evaluated in fp64 and rounded once to bf16 (nearest even).  Encodings: a bf16
+ * each output the exact value of that expression rounded once to bf16 (nearest
+ * even; the products are exact in fp64 and their sum is rounded to odd before
+ * the bf16 step).  Encodings: a bf16
  * output holds that bf16 value; an e4m3 output holds the OCP e4m3 code of
  * value / scale (IEEE fp32 division, magnitudes above 448 saturate to 448,
  * nearest even), with q_scale for q_out and kv_scale for the cache (the

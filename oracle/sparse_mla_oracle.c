@@ -241,19 +241,50 @@ uint16_t oracle_bf16_round(double v) {
   return sign | (uint16_t)((w >> 16) & 0x7FFF);
 }
 
+/* Nearest bf16 to the exact sum a + b of two doubles, ties to even.  The sum
+ * is first split exactly into hi + lo (Knuth's TwoSum: hi = the double nearest
+ * to a + b, lo the exact remainder, |lo| <= half an ulp of hi).  In units of
+ * the bf16 spacing q at |hi|, hi / q = n + f with n an integer and f in [0, 1)
+ * (both exact); the exact sum is above the midpoint between n q and (n + 1) q
+ * exactly when f - 1/2 + lo / q > 0.  A non-zero f - 1/2 is a multiple of an
+ * ulp of hi / q, larger than |lo / q|, so it decides alone; at f = 1/2 the sign
+ * of lo decides, and only lo = 0 is a tie.  Rounding hi alone would round
+ * twice (fp64, then bf16) and can land on the wrong side of a midpoint. */
+static uint16_t bf16_round_sum(double a, double b) {
+  const double hi = a + b;
+  const double bb = hi - a;
+  const double lo = (a - (hi - bb)) + (b - bb);
+  if (isnan(hi) || isinf(hi) || lo == 0.0) return oracle_bf16_round(hi);
+  const uint16_t sign = signbit(hi) ? 0x8000 : 0x0000;
+  const double ahi = fabs(hi), alo = signbit(hi) ? -lo : lo;   /* |a + b| = ahi + alo */
+  int e;
+  frexp(ahi, &e);
+  int qexp = e - 8;
+  if (qexp < -133) qexp = -133;
+  const double h = ldexp(ahi, -qexp);
+  const double n = floor(h);
+  const double f = h - n;
+  int up;
+  if (f != 0.5) up = f > 0.5;
+  else up = alo > 0.0;
+  const double r = ldexp(n + (up ? 1.0 : 0.0), qexp);
+  return sign | (oracle_bf16_round(r) & 0x7FFF);   /* r is a bf16 number (or past the largest) */
+}
+
 /* RoPE of one 64-column bf16 row at one position, as bf16 bits.  Pairs are
  * (i, i + 32) for the rotate-halves ("neox") form and (2i, 2i + 1) for the
  * interleaved form; pair i turns by the angle whose cosine / sine are
- * cs[i] / cs[32 + i]: (x, y) -> (x cos - y sin, y cos + x sin), formed in fp64
- * (both products exact) and rounded once to bf16. */
+ * cs[i] / cs[32 + i]: (x, y) -> (x cos - y sin, y cos + x sin), each output
+ * the exact value rounded once to bf16 (the products of a bf16 and an fp32
+ * number are exact in fp64, the sum is taken exactly by bf16_round_sum). */
 static void rope_row(const uint16_t* x, const float* cs, int is_neox, uint16_t* out) {
   for (int i = 0; i < 32; ++i) {
     const int ix = is_neox ? i : 2 * i;
     const int iy = is_neox ? i + 32 : 2 * i + 1;
     const double c = cs[i], s = cs[32 + i];
     const double xv = oracle_bf16_value(x[ix]), yv = oracle_bf16_value(x[iy]);
-    out[ix] = oracle_bf16_round(xv * c - yv * s);
-    out[iy] = oracle_bf16_round(yv * c + xv * s);
+    out[ix] = bf16_round_sum(xv * c, -(yv * s));
+    out[iy] = bf16_round_sum(yv * c, xv * s);
   }
 }
 

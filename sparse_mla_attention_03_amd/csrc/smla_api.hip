@@ -153,7 +153,13 @@ smla_status_t varlen_layout(int64_t T, int64_t H, VarlenLayout* L) {
   if (st != SMLA_OK) return st;
   const int64_t HG = H / smla::heads_per_workgroup(H);
   const int64_t per = (cus + HG - 1) / HG;
-  const int64_t U = T + per + 1, P = 2 * per + 1;
+  int64_t U = T + per + 1;
+  const int64_t P = 2 * per + 1;
+  // a smaller unit table, for tests of what a dropped unit does (never larger)
+  if (const char* cap = getenv("SPARSEMLA_TEST_UNIT_TABLE")) {
+    const long long c = atoll(cap);
+    if (c >= 1 && c < U) U = c;
+  }
   L->max_units = (int32_t)U;
   L->max_prows = (int32_t)P;
   L->HG = (int32_t)HG;
@@ -462,7 +468,7 @@ smla_status_t sparse_mla_rope_concat_cache(const void* ql_nope, int64_t ql_strid
     return fail(SMLA_ERR_DTYPE, "q_out_dtype=%d / kv_dtype=%d unknown", q_out_dtype, kv_dtype);
   if (!(q_scale > 0.0f && std::isfinite(q_scale)) || !(kv_scale > 0.0f && std::isfinite(kv_scale)))
     return fail(SMLA_ERR_INVALID_ARG, "q_scale and kv_scale must be positive and finite");
-  if (T * (H + 1) * 72 > 0xffffffffLL)
+  if (T > 0 && H + 1 > 0xffffffffLL / (72 * T))   // T (H + 1) 72 > 2^32 - 1, without forming the product
     return fail(SMLA_ERR_UNSUPPORTED, "T=%lld x H=%lld is beyond one launch (T*(H+1)*72 < 2^32)",
                 (long long)T, (long long)H);
   if (T == 0) return SMLA_OK;

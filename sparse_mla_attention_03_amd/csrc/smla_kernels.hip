@@ -1641,6 +1641,17 @@ __global__ __launch_bounds__(kThreads) void smla_combine_kernel(FwdParams p) {
     fr = __builtin_amdgcn_readfirstlane(p.tok_first[t]);
     rs = 1;
     cnt = __builtin_amdgcn_readfirstlane(p.tok_count[t]);
+    if (__builtin_amdgcn_readfirstlane(p.num_units[1]) != 0) {
+      // the plan dropped units (its bounds exclude this): every output of the
+      // call becomes NaN rather than whatever the buffers held
+      for (int i = threadIdx.x; i < 128 * CPT; i += kThreads) {
+        const int h = i / (8 * CPT), k8 = i - h * (8 * CPT);
+        *reinterpret_cast<u32x4*>(p.out + ((int64_t)t * p.H + 16 * grp + h) * kDV + 64 * CPT * slice + 8 * k8) =
+            u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+      }
+      if (slice == 0 && cl == 0) p.lse[(int64_t)t * p.H + head] = __builtin_nanf("");
+      return;
+    }
     if (cnt == 1) return;   // the token's only unit wrote out / lse itself
     cnt = max(0, min(cnt, p.max_prows - fr));
   }
@@ -1744,8 +1755,12 @@ __global__ __launch_bounds__(kThreads) void smla_quantize_q_kernel(const uint16_
 // the device once; token t gets count_t = max(1, ceil(len_t / R)) of them.
 // Units are numbered token by token; the units of split tokens (count > 1) get
 // consecutive partial rows, a token's only unit gets -1 (it writes out / lse
-// itself).  Bounds (checked by the writes): units <= T + CUs / HG, partial
-// rows < 2 CUs / HG.
+// itself).  Bounds: count_t <= 1 + tiles_t / rt, so units <= T + W / rt <=
+// T + CUs / HG; a split token has tiles_t > rt, so count_t <= 2 tiles_t / rt
+// and partial rows <= 2 W / rt <= 2 CUs / HG.  The host sizes the tables one
+// past these.  Every write is still checked against the table sizes; a unit
+// that would not fit is dropped with all units after it, and num_units[1] is
+// set, on which the combine kernel writes NaN to every output of the call.
 __device__ __forceinline__ int block_sum_1024(int v, int* s_part) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -1804,7 +1819,10 @@ __global__ __launch_bounds__(1024) void smla_plan_kernel(PlanParams q) {
     __syncthreads();
   }
   __syncthreads();
-  if (tid == 0) *q.num_units = min(min(s_carry[0], q.max_units), s_cut);
+  if (tid == 0) {
+    *q.num_units = min(min(s_carry[0], q.max_units), s_cut);
+    q.num_units[1] = s_cut != 0x7fffffff ? 1 : 0;   // read by the combine kernel
+  }
 }
 
 hipError_t launch_plan(const PlanParams& q, hipStream_t stream) {

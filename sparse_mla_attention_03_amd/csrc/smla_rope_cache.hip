@@ -18,12 +18,15 @@
 // 8K - 33K rows and saves 6 - 8 % from 70K rows).  The rotation:
 //   (x, y) -> (x cos - y sin, y cos + x sin)
 // with the pairs (i, i + 32) (rotate-halves, "neox") or (2i, 2i + 1)
-// (interleaved).  The rotation is evaluated in fp64 -- both products are exact
-// for a bf16 times an fp32, so one rounding happens, at the difference -- and
-// rounded once to bf16 on the fp64 bits; a chunk with an output outside the
-// range of normal bf16 numbers (zero, subnormal, non-finite) takes a two-step
-// conversion instead (to fp32 with round-to-odd, which keeps the final
-// round-to-nearest-even exact).  e4m3 outputs encode value / scale (the
+// (interleaved).  Each output is the exact value rounded once to bf16: both
+// products are exact in fp64 for a bf16 times an fp32, their sum is rounded
+// to fp64 with round-to-odd (the exact error of the nearest-rounded sum, from
+// TwoSum, moves an even result one step toward the exact value), and the
+// round-to-odd fp64 value, with 45 bits more than bf16, rounds to nearest even
+// as the exact value would.  The bf16 step works on the fp64 bits; a chunk
+// with an output outside the range of normal bf16 numbers (zero, subnormal,
+// non-finite) takes a two-step conversion instead (to fp32 with round-to-odd,
+// then to bf16).  e4m3 outputs encode value / scale (the
 // correctly rounded fp32 quotient, saturated to +-448, round to nearest even)
 // of the bf16 value.
 #include <hip/hip_runtime.h>
@@ -40,6 +43,21 @@ constexpr int kLatentRows = 4;   // rows per latent wave
 constexpr uint32_t kGroup = 8 / kLatentRows + 1;   // waves per group: latent ones, then one rope wave
 constexpr int64_t kInterleaveRows = 49152;          // rows from which the wave kinds interleave
 static_assert(8 % kLatentRows == 0, "a group covers the eight rows of its rope wave");
+
+// a + b for two fp64 values whose exact sum is wanted, rounded to odd: the
+// nearest sum s and its exact error (Knuth's TwoSum, six additions; a and b
+// are exact products, so contracting one of them into an addition rounds the
+// same way); a non-zero error on
+// an s with an even last bit moves s one ulp toward the exact sum (up in
+// magnitude when the error has s's sign), which is the round-to-odd result.
+__device__ __forceinline__ double add_round_odd(double a, double b) {
+  const double s = a + b;
+  const double bb = s - a;
+  const double err = (a - (s - bb)) + (b - bb);
+  uint64_t u = (uint64_t)__double_as_longlong(s);
+  if (err != 0.0 && (u & 1u) == 0u) u += ((err > 0.0) == (s > 0.0)) ? 1u : ~(uint64_t)0;
+  return __longlong_as_double((long long)u);
+}
 
 // fp64 -> bf16 bits, round to nearest even, in two steps that round once: to
 // fp32 toward zero with the sticky "inexact" bit folded into the last place
@@ -132,7 +150,7 @@ __device__ __forceinline__ void rope8(const uint16_t* x, const float* cs, int j,
     for (int i = 0; i < 8; ++i) {
       const double c = cs[f0 + i], s = cs[32 + f0 + i];
       const double a = own[i], b = other[i];
-      d[i] = first ? a * c - b * s : a * c + b * s;
+      d[i] = add_round_odd(a * c, first ? -(b * s) : b * s);
     }
   } else {
     // pairs (2m, 2m + 1), frequency m
@@ -141,8 +159,8 @@ __device__ __forceinline__ void rope8(const uint16_t* x, const float* cs, int j,
       const int m = 4 * j + i;
       const double c = cs[m], s = cs[32 + m];
       const double a = own[2 * i], b = own[2 * i + 1];
-      d[2 * i] = a * c - b * s;
-      d[2 * i + 1] = b * c + a * s;
+      d[2 * i] = add_round_odd(a * c, -(b * s));
+      d[2 * i + 1] = add_round_odd(b * c, a * s);
     }
   }
   bool ok = true;

@@ -212,3 +212,18 @@ def test_ceiling_library_exports_its_header():
                                              ctypes.c_int64, ctypes.c_void_p]
     assert lib.smla_ceiling_stream_read(None, 1 << 20, None, 0, None) == 1
     assert lib.smla_ceiling_stream_read(P, 1 << 20, P, 16, None) == 2
+
+
+def test_rope_entry_size_guard_does_not_overflow(lib):
+    """T (H + 1) 72 bytes must stay below 2^32 for one launch; T and H up to
+    2^31 - 1 would overflow that product in 64 bits if it were formed."""
+    def call(T, H, ql=P):
+        return lib.sparse_mla_rope_concat_cache(ql, 576, 576, P, 64, 64, P, 512, P, 64, P, P, 4096, 1, T, H,
+                                                P, 0, 1.0, P, P, 0, 1, 64, 1.0, None)
+    big = 0x7FFFFFFF
+    assert call(big, big) == UNSUP
+    assert call(1000, 10_000_000) == UNSUP
+    assert call(big, 1) == UNSUP
+    assert call(0, big) == OK                     # nothing to do: a no-op
+    assert call(2, 16, ql=None) == NULL           # within the guard: the next check decides
+    assert call(big // 100, 16, ql=None) == UNSUP

@@ -120,7 +120,7 @@ def test_fused_outputs_feed_the_forward_pass():
 # finite bf16, the smallest normal one and 2^-100 (so that products reach the
 # subnormal range), and a value one step above 1
 _EDGE_BF16 = np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x4000, 0xC000, 0x4040, 0x3F81, 0x0D80, 0x0080,
-                       0x7F7F, 0xFF7F, 0x3F00], dtype=np.uint16)
+                       0x7F7F, 0xFF7F, 0x3F00, 0x2180, 0xA180], dtype=np.uint16)
 
 
 def _edge_table():
@@ -128,9 +128,9 @@ def _edge_table():
     bf16 rounding has to get right: exact bf16 midpoints with a tiny second
     product pushing them either way (or not at all), subnormal and underflowing
     outputs, overflow to infinity, exact zeros, and plain angles."""
-    cs = np.empty((8, 64), np.float32)
+    cs = np.empty((9, 64), np.float32)
     rows = [(1.0, 0.0), (0.5 + 2.0 ** -9, 2.0 ** -40), (2.0 ** -30, 2.0 ** -31), (0.75, 0.75),
-            None, (1.0 - 2.0 ** -24, 2.0 ** -12), (0.0, 1.0), (0.999, -0.0447)]
+            None, (1.0 - 2.0 ** -24, 2.0 ** -12), (0.0, 1.0), (0.999, -0.0447), (511.0 / 512.0, 0.5)]
     real = synth.rope_cos_sin(4096)[1234]
     for p, r in enumerate(rows):
         if r is None:
@@ -152,9 +152,31 @@ def test_fused_rope_cache_rounding_edge_values(is_neox, q_fp8, kv_fp8):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
 
     case = replace(case, q_pe=edge((T, H, 64)), k_pe=edge((T, 64)),
-                   positions=torch.arange(T, dtype=torch.int64) % 8,
+                   positions=torch.arange(T, dtype=torch.int64) % 9,
                    cos_sin=torch.from_numpy(_edge_table()))
     _check(case, is_neox, q_fp8, kv_fp8, q_scale=1.0, kv_scale=1.0)
+
+
+@pytest.mark.parametrize("is_neox", [True, False])
+def test_fused_rope_cache_midpoint_pushed_by_a_tiny_product(is_neox):
+    """x cos on a bf16 midpoint (x = 1, cos = 511/512) with y sin = +-2^-61 or 0
+    beside it: the exact value rounds to 0x3F7F, 0x3F80 and (the tie) 0x3F80,
+    which the oracle returns; rounding to fp64 first gives 0x3F80 every time."""
+    T, H = 4, 16
+    case = synth.make_rope_case(T=T, H=H, num_blocks=1, block_size=64, seed=33)
+    ys = (0x2180, 0xA180, 0x0000)
+    qp = np.zeros((T, H, 64), np.uint16)
+    kp = np.zeros((T, 64), np.uint16)
+    for i in range(32):
+        ix, iy = (i, i + 32) if is_neox else (2 * i, 2 * i + 1)
+        qp[..., ix], kp[:, ix] = 0x3F80, 0x3F80
+        qp[..., iy], kp[:, iy] = ys[i % 3], ys[(i + 1) % 3]
+    cs = np.zeros((1, 64), np.float32)
+    cs[:, :32], cs[:, 32:] = 511.0 / 512.0, 0.5
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    case = replace(case, q_pe=bf(qp), k_pe=bf(kp), positions=torch.zeros(T, dtype=torch.int64),
+                   cos_sin=torch.from_numpy(cs))
+    _check(case, is_neox, False, False, q_scale=1.0, kv_scale=1.0)
 
 
 @pytest.mark.parametrize("q_fp8,kv_fp8", [(False, False), (True, True)])

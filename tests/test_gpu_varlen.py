@@ -125,3 +125,22 @@ def test_varlen_all_empty():
     torch.cuda.synchronize()
     o = out.view(torch.int16)
     assert torch.equal(o, torch.zeros_like(o)) and bool(torch.isneginf(lse).all())
+
+
+def test_dropped_plan_units_turn_every_output_nan(monkeypatch):
+    """The plan's unit table is sized past what its unit length can produce, so
+    no unit is ever dropped.  Forced smaller from the host, the dropped units
+    must show: every output and lse of the call is NaN, not stale memory."""
+    T, H, D, K = 12, 16, 512, 700
+    case, idx, lens, _ = _mixed_case(T, H, D, K, 4096, "bf16", seed=5)
+    out = torch.zeros(T, H, 512, dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros(T, H, dtype=torch.float32, device=DEV)
+    monkeypatch.setenv("SPARSEMLA_TEST_UNIT_TABLE", "3")
+    binding.sparse_mla_fwd_varlen(case.q, case.kv_pool, idx, lens, case.sm_scale, case.kv_scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(out.float()).all()) and bool(torch.isnan(lse).all())
+    # the same call with the table at its size: finite again
+    monkeypatch.delenv("SPARSEMLA_TEST_UNIT_TABLE")
+    binding.sparse_mla_fwd_varlen(case.q, case.kv_pool, idx, lens, case.sm_scale, case.kv_scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(out.float()).any())

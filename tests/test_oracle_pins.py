@@ -28,11 +28,7 @@ from tests.helpers import bits16, codes8, kv_bits, kv_values_f64, read_golden, r
 # ---------------------------------------------------------------- codecs
 
 def test_bf16_decode_all_patterns():
-    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
-    # sample every 7th pattern plus the special ones (full sweep is slow via ctypes)
-    sel = np.unique(np.concatenate([pats[::7], np.array([0, 0x8000, 0x7F80, 0xFF80, 0x7F7F,
-                                                         0x0001, 0x8001, 0x3F80, 0xBF80],
-                                                        dtype=np.uint16)]))
+    sel = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)   # every pattern
     ours = oracle.bf16_value(sel)
     ref = torch.from_numpy(sel.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     nan = np.isnan(ref)

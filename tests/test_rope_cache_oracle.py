@@ -95,6 +95,40 @@ def test_rotation_exact(is_neox):
         assert np.array_equal(cache[slot, :512], bits16(case.kv_c)[t])
 
 
+@pytest.mark.parametrize("is_neox", [True, False])
+def test_rotation_rounds_the_exact_value_once(is_neox):
+    """x = 1 and cos = 511/512 put x cos exactly on the midpoint between the
+    bf16 numbers 1 - 2^-8 (0x3F7F) and 1 (0x3F80); a second product y sin of
+    +-2^-61 moves the exact value just below or just above it, by far less than
+    half an fp64 ulp.  The exact value rounds to 0x3F7F / 0x3F80; rounding it to
+    fp64 first would land on the midpoint and tie to 0x3F80 both times.  With
+    y = 0 the value is the midpoint itself and ties to the even 0x3F80."""
+    case = _case(T=2, H=2, seed=4)
+    T, H = 2, 2
+    ys = {0: 0x2180, 1: 0xA180, 2: 0x0000}          # +2^-60, -2^-60, 0
+    want_x = {0: 0x3F7F, 1: 0x3F80, 2: 0x3F80}
+    qp = np.zeros((T, H, 64), np.uint16)
+    for i in range(32):
+        ix, iy = (i, i + 32) if is_neox else (2 * i, 2 * i + 1)
+        qp[:, :, ix] = 0x3F80
+        qp[:, :, iy] = ys[i % 3]
+    cs = np.zeros((512, 64), np.float32)
+    cs[:, :32] = 511.0 / 512.0
+    cs[:, 32:] = 0.5
+    q_pe = torch.from_numpy(qp.view(np.int16)).view(torch.bfloat16)
+    case = synth.RopeCase(case.ql_nope, q_pe, case.kv_c, case.k_pe, case.positions, torch.from_numpy(cs),
+                          case.slot_mapping, case.num_blocks, case.block_size)
+    q, _ = _run(case, is_neox)
+    for t in range(T):
+        for h in range(H):
+            for i in range(32):
+                ix, iy = (i, i + 32) if is_neox else (2 * i, 2 * i + 1)
+                assert q[t, h, 512 + ix] == want_x[i % 3], (t, h, i, hex(int(q[t, h, 512 + ix])))
+                a, b = _bf16_exact(0x3F80), _bf16_exact(ys[i % 3])
+                ey = b * Fraction(511, 512) + a * Fraction(1, 2)
+                assert q[t, h, 512 + iy] == _nearest_bf16(ey, float(ey))
+
+
 def test_zero_angle_is_the_plain_concat():
     case = _case(T=4, H=3, seed=2)
     cs = np.zeros((512, 64), np.float32)
