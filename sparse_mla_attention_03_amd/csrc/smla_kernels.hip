@@ -38,10 +38,6 @@
 
 namespace smla {
 
-#ifndef SMLA_QB_DEPTH
-#define SMLA_QB_DEPTH 1
-#endif
-
 template <bool KV8, int DQK, int HT, bool QB = false>
 __global__ __launch_bounds__(kThreads, 1) void smla_tiles_kernel(FwdParams p) {
   using G = Geom<KV8, DQK>;
@@ -1044,14 +1040,16 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
   static_assert(!QB || KV8, "bf16 dots are an e4m3-KV variant");
   constexpr bool F8 = KV8 && !QB;
   constexpr int NKQ = F8 ? G::NKB : DQK / 32;   // QK k-steps
-  constexpr int TR = KV8 ? 64 : 32;        // rows per tile (36 KiB for Dqk = 576 either way)
+  // rows per tile: 36 KiB for Dqk = 576 with e4m3 dots or bf16 KV; 32 rows (18 KiB) for bf16
+  // dots on e4m3 KV, whose score waves hold q as bf16 and have no registers for more
+  constexpr int TR = (KV8 && !QB) ? 64 : 32;
   constexpr int NB = TR / 16;              // 16-row QK blocks per tile
   constexpr int NKS = TR / 32;             // 32-row PV k-steps per tile
   constexpr int RPW = TR / 4;              // rows each score wave gathers (8 or 16)
   constexpr int NGRP = RPW / 8;            // 8-row load groups
   constexpr int NCI = G::MAIN / 128;       // 128-byte pieces of a row's V part
   constexpr int NLDM = NGRP * NCI;
-  constexpr int TROWS = (G::TCH == 8) ? 8 : 16;      // RoPE part: rows per load
+  constexpr int TROWS = (G::TCH == 8 || RPW < 16) ? 8 : 16;   // RoPE part: rows per load
   constexpr int NLDT = G::TCH ? RPW / TROWS : 0;
   constexpr int NLD = NLDM + NLDT;
   constexpr int TMAIN = TR * G::MAIN;
@@ -1164,8 +1162,9 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
       if constexpr (NLDT > 0) {
 #pragma unroll
         for (int j = 0; j < NLDT; ++j)
-          *reinterpret_cast<u32x4*>(st + off_tail(RPW * qw + TROWS * j + lane / G::TCH, lane % G::TCH)) =
-              ld[NLDM + j];
+          if (lane / G::TCH < TROWS)   // e4m3 parts of 8 rows: lanes 32-63 load zeros and store nothing
+            *reinterpret_cast<u32x4*>(st + off_tail(RPW * qw + TROWS * j + lane / G::TCH, lane % G::TCH)) =
+                ld[NLDM + j];
       }
       if (lane == 0) s_mask[stage][qw] = vm;
     };
@@ -1325,9 +1324,9 @@ __global__ __launch_bounds__(2 * kThreads) void smla_heads_kernel(FwdParams p) {
     // DEPTH k-steps ahead of their MFMA (LDS latency) and each block keeps two
     // partial sums (even / odd k-steps), so back-to-back MFMAs are
     // independent.  e4m3: the four blocks already are.
-    // QB: four row blocks are four independent chains already, and its bf16 q
-    // fragments leave fewer registers for reads in flight
-    constexpr int DEPTH = QB ? SMLA_QB_DEPTH : 3;
+    // QB: one partial sum per row block (its bf16 q takes the registers of the
+    // second); with 32-row tiles its two blocks alternate
+    constexpr int DEPTH = 3;
     constexpr int NACC = QB ? 1 : 2;
     auto qk = [&](const uint8_t* st, f32x4 (&acc)[NB]) {
       if constexpr (F8) {
