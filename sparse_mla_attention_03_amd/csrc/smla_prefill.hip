@@ -1,17 +1,35 @@
 // smla_prefill.hip -- 16-head groups on whole long lists (prefill) of bf16 rows
 // 512 wide.
 //
-// Each wave streams its own 16-row tiles (tiles wave, wave + 4, ...) through a
-// private LDS slot, with no barrier in the loop, as the 16-head kernel of
-// smla_kernels.hip does; the difference is how rows reach LDS.  Every row is
-// copied from the pool straight into the slot by one global_load_lds_dwordx4
-// (64 lanes x 16 bytes, its 16-byte chunks permuted by the row number through
-// the lane offsets), with the slot ids of a tile coming in by one scalar
-// buffer load, so a tile in flight holds no registers and needs no ds_write.
-// That frees enough registers for two workgroups per compute unit (two waves
-// per SIMD): while one wave waits for its next tile, the other computes.  LDS
-// per workgroup is exactly 80 KiB: four 16 KiB slots and q (16 rows of 1 KiB,
-// read by all four waves as the B operand of QK^T).
+// Each wave takes every fourth 16-entry tile of its token's list (tiles wave,
+// wave + 4, ...) and streams them through a private LDS slot with no barrier
+// in the loop.  Three things set this kernel apart from the 16-head kernel of
+// smla_kernels.hip:
+//
+// * Entry order.  Many query rows of one sequence select overlapping rows of
+//   a pool a few MiB large, so whether a gathered row is still in L2 depends
+//   on when the waves of an XCD read it.  Before its loop each wave orders its
+//   share of the list (up to 512 entries per round) by slot range: a stable
+//   split on three bits of the slot id (eight ranges over the pool) and a
+//   fourth split that moves invalid entries (padding, ids outside the pool)
+//   past the valid ones, where they are dropped.  All resident waves then
+//   sweep the pool from low to high slots at about the same pace, and a
+//   range of the pool is read by all of them while it is in L2.  The order is
+//   a function of the list alone (equal keys keep their list order), so the
+//   result is deterministic; softmax does not depend on the order.
+//   The sorted ids stay in registers (8 per lane); each tile's ids reach the
+//   lanes that need them by one cross-lane permute per 8 rows.
+// * Copies.  Rows go from the pool straight into LDS by global_load_lds_dwordx4,
+//   8 rows x 128 bytes per copy (lane l: row l >> 3, one 16-byte chunk), so a
+//   64-bit lane address is formed once per 8 rows and the eight copies of
+//   those rows differ only in their immediate offset; per copy only M0 is
+//   set.  In the slot, chunk c of row r sits at byte
+//   8192 (r >> 3) + 1024 (c >> 3) + 128 (r & 7) + 16 ((c & 7) ^ kx(r)),
+//   kx(r) = (r >> 1) & 7: every copy fills 1 KiB lane-linearly, and 16 rows
+//   read at one chunk hit 16 different 16-byte bank groups.
+// * Two workgroups per compute unit (two waves per SIMD): LDS per workgroup is
+//   exactly 80 KiB, four 16 KiB slots and q (16 rows of 1 KiB, read by all
+//   four waves as the B operand of QK^T).
 //
 // Per tile: QK^T on 16x16x32 bf16 MFMAs (S^T[row][head], fragments read three
 // k-steps ahead), the online softmax with a lazily moved reference max, and PV
@@ -24,6 +42,27 @@
 
 namespace smla {
 
+namespace {
+
+// global_load_lds_dwordx4 from a per-lane 64-bit address plus the immediate
+// OFF.  The immediate offsets the LDS destination as well, so M0 is set to
+// the wanted destination minus OFF (M0 needs one wait state after it is
+// written).  The add that forms M0 writes SCC: declared, so that no compare
+// the compiler keeps in SCC lives across a copy.
+template <int OFF, int LDS>
+__device__ __forceinline__ void copy_v_off(const uint8_t* src, uint32_t slot_lds) {
+  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%3" ::"v"(src),
+               "s"(slot_lds), "i"(LDS - OFF), "i"(OFF)
+               : "memory", "m0", "scc");
+}
+
+// lanes below this one with their bit set in m
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+}  // namespace
+
 __global__ __launch_bounds__(kThreads, 2) void smla_prefill_kernel(FwdParams p) {
   using G = Geom<false, 512>;
   constexpr int TR = 16;                       // rows per tile
@@ -32,7 +71,10 @@ __global__ __launch_bounds__(kThreads, 2) void smla_prefill_kernel(FwdParams p) 
   constexpr int LDS = QOFF + 16 * G::MAIN;     // 80 KiB: two workgroups per compute unit
   constexpr int NKQ = 16;                      // QK k-steps (32 columns each)
   constexpr int OP = 256 + 4;                  // merge row: two quarters of fp32, padded
+  constexpr int NREG = 8;                      // a wave's entries per round: NREG x 64 (32 tiles)
+  constexpr int RTILES = NREG * 64 / TR;
   static_assert(4 * 16 * OP * 4 + 2 * 64 * 4 <= LDS, "merge buffer fits");
+  static_assert(NREG * 64 * 4 <= SLOT, "the sort scratch fits in a slot");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
 
@@ -51,64 +93,145 @@ __global__ __launch_bounds__(kThreads, 2) void smla_prefill_kernel(FwdParams p) 
   if (!unit_of(p, u, wu)) return;
   const int t = wu.t;
   const int h0 = hg * 16;
-  const int kbeg = wu.kbeg;
-  const int kend = wu.kend;
-  const int ntile = kend > kbeg ? (kend - kbeg + TR - 1) / TR : 0;
-  const int nt = ntile > wave ? (ntile - wave + 3) / 4 : 0;   // this wave's tiles: wave + 4i
+  const int len = wu.kend > wu.kbeg ? wu.kend - wu.kbeg : 0;
+  const int ntile = (len + TR - 1) / TR;
+  const int ntw = ntile > wave ? (ntile - wave + 3) / 4 : 0;   // this wave's tiles: wave + 4i
+  const int nround = (ntw + RTILES - 1) / RTILES;
   const int head = h0 + m16;
 
   uint8_t* slot = smem + wave * SLOT;
   const uint32_t slot_lds = lds_addr(slot);
   const uint8_t* qs = smem + QOFF;
+  int32_t* sscr = reinterpret_cast<int32_t*>(slot);   // sort scratch (before a round's copies)
 
-  // ---- slot ids of this wave's tile i (16 entries) through the scalar unit
-  const i32x4 ids_rsrc = scalar_rsrc(p.idx + (int64_t)t * p.idx_st + kbeg, 4 * (kend - kbeg));
-  auto load_ids = [&](int i) -> i32x16 { return sbuf_load_x16(ids_rsrc, 4 * TR * (wave + 4 * i), 0); };
+  // ---- the wave's share of round rd: entry j = 64k + l (register k, lane l) is
+  // row j & 15 of wave tile 32 rd + (j >> 4), i.e. list position
+  // 16 (wave + 4 (32 rd + (j >> 4))) + (j & 15); -1 past the list
+  const __amdgpu_buffer_rsrc_t ids_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.idx + (int64_t)t * p.idx_st + wu.kbeg), (short)0, (int)(4 * len), kBufferRsrcWord3);
   // a slot id is valid when 0 <= id < N: one unsigned compare against min(N, 2^31)
   const uint32_t n_lim = (uint32_t)min(p.N, (int64_t)0x80000000LL);
-  const uint8_t* zero_row = g_zero_row;
-  // 16 copies: row r of tile i into slot row r, lane l fetching chunk l ^ row_key(r);
-  // returns the validity bits of the tile's rows
-  const uint32_t lane16 = 16 * lane;
-  auto issue = [&](int i, const i32x16& ids) -> uint32_t {
-    const int k0 = kbeg + TR * (wave + 4 * i);
-    uint32_t vm = 0;
-    static_for<0, TR>([&](auto rc) {
-      constexpr int r = decltype(rc)::value;
-      const bool ok = (uint32_t)ids[r] < n_lim && k0 + r < kend;
-      vm |= ok ? (1u << r) : 0u;
-      const uint8_t* b = ok ? p.kv + (uint64_t)(uint32_t)ids[r] * G::ROW : zero_row;
-      copy_sx<16 * row_key(r)>(b, lane16, slot_lds + r * G::MAIN);
-    });
-    return vm;
+  // slot ranges: the top three bits of the smallest power of two >= N
+  const int lg = n_lim > 1 ? 32 - __builtin_clz(n_lim - 1) : 0;
+  const int rsh = lg > 3 ? lg - 3 : 0;
+  int32_t sid[NREG];
+  auto load_round = [&](int rd) {
+#pragma unroll
+    for (int k = 0; k < NREG; ++k) {
+      const int pos = TR * (wave + 4 * (RTILES * rd + 4 * k + (lane >> 4))) + m16;
+      const int v = raw_load_b32(ids_rsrc, 4 * pos, 0, 0);
+      sid[k] = pos < len ? v : -1;
+    }
+  };
+  // stable split of the NREG x 64 entries (in order j) on bit b of their key
+  // (bits 0-2: slot range, bit 3: invalid) through the wave's LDS scratch;
+  // returns the number of entries whose bit is clear
+  auto split = [&](int b) -> int {
+    uint64_t ones[NREG];
+    bool one[NREG];
+    int before[NREG];
+    int n1 = 0;
+#pragma unroll
+    for (int k = 0; k < NREG; ++k) {
+      const uint32_t id = (uint32_t)sid[k];
+      const uint32_t key = id < n_lim ? ((id >> rsh) & 7u) : 8u;
+      one[k] = (key >> b) & 1u;
+      ones[k] = __ballot(one[k]);
+      before[k] = n1;
+      n1 += __popcll(ones[k]);
+    }
+    const int n0 = NREG * 64 - n1;
+#pragma unroll
+    for (int k = 0; k < NREG; ++k) {
+      const int o = lanes_below(ones[k]);
+      const int pos = one[k] ? n0 + before[k] + o : 64 * k - before[k] + lane - o;
+      sscr[pos] = sid[k];
+    }
+#pragma unroll
+    for (int k = 0; k < NREG; ++k) sid[k] = sscr[64 * k + lane];
+    return n0;
+  };
+  auto sort_round = [&]() -> int {
+    split(0);
+    split(1);
+    split(2);
+    const int nvalid = split(3);
+    wait_lgkmcnt0();   // the scratch reads are done before copies land in the slot
+    return nvalid;
   };
 
-  // ---- q: wave w copies heads 4w .. 4w + 3 (row h, chunk c at c ^ row_key(h)),
-  // then the first tile; q has landed once only the tile's copies are outstanding
+  // ---- copies of tile i (of the round): lane l copies row 8 gr + (l >> 3) for
+  // gr = 0, 1, its 16-byte chunk (l & 7) ^ kx(row) of each 128-byte piece j
+  // into slot byte 1024 (8 gr + j) + 16 l
+  const uint32_t key16[2] = {16u * (uint32_t)((lane & 7) ^ (lane >> 4)),
+                             16u * (uint32_t)((lane & 7) ^ (4 + (lane >> 4)))};
+  const uint8_t* zero_row = g_zero_row;
+  // the ids of tile i's copy rows (sid[0] holds tiles 4 (i >> 2) .. + 3 then)
+  auto fetch = [&](int i, int32_t (&cid)[2]) {
+    cid[0] = __shfl(sid[0], 16 * (i & 3) + (lane >> 3));
+    cid[1] = __shfl(sid[0], 16 * (i & 3) + 8 + (lane >> 3));
+  };
+  auto rotate = [&]() {
+#pragma unroll
+    for (int k = 0; k + 1 < NREG; ++k) sid[k] = sid[k + 1];
+  };
+  int nvalid = 0;
+  auto issue = [&](int i, const int32_t (&cid)[2]) -> uint32_t {
+    static_for<0, 2>([&](auto gc) {
+      constexpr int gr = decltype(gc)::value;
+      // rows past the valid ones read the zero row; the id test keeps every
+      // address inside the pool whatever the permutes delivered
+      const bool ok = TR * i + 8 * gr + (lane >> 3) < nvalid && (uint32_t)cid[gr] < n_lim;
+      const uint8_t* rp = (ok ? p.kv + (uint64_t)(uint32_t)cid[gr] * G::ROW : zero_row) + key16[gr];
+      static_for<0, 8>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        copy_v_off<128 * j, 1024 * (8 * gr + j)>(rp, slot_lds);
+      });
+    });
+    const int nv = nvalid - TR * i;   // valid rows of the tile
+    return nv >= TR ? 0xffffu : (1u << nv) - 1u;
+  };
+
+  // ---- q: wave w copies heads 4w .. 4w + 3 (row h, chunk c at c ^ row_key(h));
+  // then the first round's ids, its order, and its first tile
   {
     const uint8_t* qtok = reinterpret_cast<const uint8_t*>(p.q + (int64_t)t * p.q_st);
-    // rows 4w + i have keys ((i & 1) << 3) | (2w + (i >> 1)): the wave's part as a scalar
+    const uint32_t lane16 = 16 * lane;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hh = 4 * wave + i;
       copy_s(qtok + (int64_t)(h0 + hh) * p.q_sh * 2, lane16 ^ (16 * row_key(hh)), lds_addr(qs) + hh * G::MAIN);
     }
   }
-  i32x16 ids = load_ids(0);
+  int nt = 0;                     // tiles of the current round
+  int32_t cid[2];
   uint32_t vm_cur = 0;
-  if (nt > 0) {
-    vm_cur = issue(0, ids);
-    wait_vmcnt<TR>();
-  } else {
-    wait_vmcnt<0>();
-  }
-  ids = load_ids(1);
+  auto start_round = [&](int rd) {
+    load_round(rd);
+    nvalid = sort_round();
+    nt = (nvalid + TR - 1) / TR;
+    if (nt > 0) {
+      fetch(0, cid);
+      vm_cur = issue(0, cid);
+      fetch(1, cid);
+    }
+  };
+  if (nround > 0) start_round(0);
+  wait_vmcnt<0>();
   __syncthreads();   // every wave's q rows are in LDS
   const float c2 = p.sm_scale * p.kv_scale * kLog2e;   // logit multiplier, log2 domain
 
-  // QK reads: row m16 (key k = row_key(m16)), chunk 4kb + g lands at
-  // 4 (kb ^ (k >> 2)) + (g ^ (k & 3)): one lane base per kb mod 4, the same
-  // for the K rows of the slot and the q rows (head m16)
+  // QK reads: lane (m16, g) at k-step kb takes chunk 4 kb + g of row m16 of the
+  // tile and of q (head m16).  Tile: byte 8192 (m16 >> 3) + 128 (m16 & 7) +
+  // 1024 (kb >> 1) + 16 ((4 (kb & 1) + g) ^ kx(m16)), two lane bases by kb & 1;
+  // q (row-major, key row_key(m16)): chunk 4kb + g at 4 (kb ^ (k >> 2)) +
+  // (g ^ (k & 3)), four lane bases by kb mod 4
+  int kq_base[2];
+  {
+    const int kx = (m16 >> 1) & 7;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) kq_base[b] = 8192 * (m16 >> 3) + 128 * (m16 & 7) + 16 * ((4 * b + g) ^ kx);
+  }
   int qk_base[4];
 #pragma unroll
   for (int r4 = 0; r4 < 4; ++r4) {
@@ -116,15 +239,19 @@ __global__ __launch_bounds__(kThreads, 2) void smla_prefill_kernel(FwdParams p) 
     qk_base[r4] = m16 * G::MAIN + 64 * (r4 ^ (k >> 2)) + 16 * (g ^ (k & 3));
   }
   // PV (transposed reads): in k-slot group g, lane k = m16 reads row
-  // 4g + (k >> 2), columns 128a + 32 (k & 3) + 4e .. +4, i.e. half e & 1 of
-  // chunk 16a + 4 (k & 3) + (e >> 1); lane (m16, g) then receives column
-  // 128a + 32 (m16 >> 2) + 4e + (m16 & 3) of rows 4g .. 4g + 3, and the output
-  // lane (head, g) holds columns 128a + 32g + 4e + i in O[a][e][i]
+  // r = 4g + (k >> 2), columns 128a + 32 (k & 3) + 4e .. +4, i.e. half e & 1 of
+  // chunk 16a + 4 (k & 3) + (e >> 1), at byte 8192 (r >> 3) + 2048 a +
+  // 1024 ((k >> 1) & 1) + 128 (r & 7) + 16 ((4 (k & 1) + (e >> 1)) ^ kx(r)) +
+  // 8 (e & 1); lane (m16, g) then receives column 128a + 32 (m16 >> 2) + 4e +
+  // (m16 & 3) of rows 4g .. 4g + 3, and the output lane (head, g) holds columns
+  // 128a + 32g + 4e + i in O[a][e][i]
   int pvt_base[4];
   {
     const int r = 4 * g + (m16 >> 2);
+    const int kx = (r >> 1) & 7;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) pvt_base[h] = r * G::MAIN + 16 * ((4 * (m16 & 3) + h) ^ row_key(r));
+    for (int h = 0; h < 4; ++h)
+      pvt_base[h] = 8192 * (r >> 3) + 1024 * ((m16 >> 1) & 1) + 128 * (r & 7) + 16 * ((4 * (m16 & 1) + h) ^ kx);
   }
 
   f32x4 O[4][8];
@@ -145,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 2) void smla_prefill_kernel(FwdParams p) 
     u32x4 ra[DEPTH], rq[DEPTH];
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
-      ra[d] = lds_read16(slot + qk_base[d & 3] + 256 * (d >> 2));
+      ra[d] = lds_read16(slot + kq_base[d & 1] + 1024 * (d >> 1));
       rq[d] = lds_read16(qs + qk_base[d & 3] + 256 * (d >> 2));
     }
 #pragma unroll
@@ -153,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 2) void smla_prefill_kernel(FwdParams p) 
       const u32x4 a = ra[kb % DEPTH], b = rq[kb % DEPTH];
       if (kb + DEPTH < NKQ) {
         const int kn = kb + DEPTH;
-        ra[kb % DEPTH] = lds_read16(slot + qk_base[kn & 3] + 256 * (kn >> 2));
+        ra[kb % DEPTH] = lds_read16(slot + kq_base[kn & 1] + 1024 * (kn >> 1));
         rq[kb % DEPTH] = lds_read16(qs + qk_base[kn & 3] + 256 * (kn >> 2));
       }
       ac[kb & 1] = mfma_bf16(a, b, ac[kb & 1]);
@@ -189,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 2) void smla_prefill_kernel(FwdParams p) 
     u32x2 A[2][8];
     auto load_a = [&](int a) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) A[a & 1][e] = lds_read_tr16(slot + pvt_base[e >> 1] + 8 * (e & 1) + 256 * a);
+      for (int e = 0; e < 8; ++e) A[a & 1][e] = lds_read_tr16(slot + pvt_base[e >> 1] + 8 * (e & 1) + 2048 * a);
     };
     load_a(0);
 #pragma unroll
@@ -208,35 +335,41 @@ __global__ __launch_bounds__(kThreads, 2) void smla_prefill_kernel(FwdParams p) 
       }
   };
 
-  // ---- the next tile goes into the slot once every read of this one is done
+  // ---- the next tile goes into the slot once every read of this one is done;
+  // then the ids of the tile after it are fetched (sid[0] moves on every 4 tiles)
   auto next = [&](int i) {
     wait_lgkmcnt0();
     if (i + 1 < nt) {
-      vm_cur = issue(i + 1, ids);
-      ids = load_ids(i + 2);
+      vm_cur = issue(i + 1, cid);
+      if (((i + 2) & 3) == 0) rotate();
+      fetch(i + 2, cid);
     }
   };
 
-  // ---- main loop.  m_run is a reference max that may lag the true one by up
-  // to kSlack, so exponents stay <= 2^kSlack; a head with no valid entry yet
-  // takes the tile's max (its O is still zero).  Only when a head's scores
-  // outgrow a finite reference is O rescaled (a uniform branch, rarely taken).
-  for (int i = 0; i < nt; ++i) {
-    wait_vmcnt<0>();   // tile i's copies (the only vector memory operations in flight)
-    score(vm_cur);
-    if (__ballot(m_run != -INFINITY && mt > m_run + kSlack) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+  // ---- main loop, by rounds of up to RTILES tiles per wave.  m_run is a
+  // reference max that may lag the true one by up to kSlack, so exponents stay
+  // <= 2^kSlack; a head with no valid entry yet takes the tile's max (its O is
+  // still zero).  Only when a head's scores outgrow a finite reference is O
+  // rescaled (a uniform branch, rarely taken).
+  for (int rd = 0; rd < nround;) {
+    for (int i = 0; i < nt; ++i) {
+      wait_vmcnt<0>();   // tile i's copies (the only vector memory operations in flight)
+      score(vm_cur);
+      if (__ballot(m_run != -INFINITY && mt > m_run + kSlack) != 0) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) O[a][e] *= alpha;
+          for (int e = 0; e < 8; ++e) O[a][e] *= alpha;
+      }
+      m_run = (m_run == -INFINITY) ? mt : m_run;
+      accumulate();
+      next(i);
     }
-    m_run = (m_run == -INFINITY) ? mt : m_run;
-    accumulate();
-    next(i);
+    if (++rd < nround) start_round(rd);
   }
 
   // ---- merge the four waves through LDS: (max, sum) of every wave, then two

@@ -363,6 +363,8 @@ PREFILL16 = [
     (1, 300, 4096, 0.2, False, False),    # ragged last tile, padding anywhere
     (1, 1100, 8192, 0.0, True, True),     # sinks, strided q
     (3, 257, 2048, 0.1, True, False),     # three 16-head groups per token
+    (1, 4100, 16384, 0.3, False, False),  # three rounds of entries per wave, padding dropped
+    (1, 2048, 2048, 0.0, False, False),   # every slot of the pool in every list
 ]
 
 
@@ -391,6 +393,10 @@ def test_whole_lists_two_workgroups_per_cu(HG, K, ctx, pad, with_sinks, strided)
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle_for_tokens(case, idx=idx, sinks=sinks)
     compare(out, lse, ref_out, ref_lse, "bf16", f"whole lists T{T} H{H} K{K}")
+    # the entry order the kernel works in is a function of the list: repeatable
+    out2, lse2 = sparse_mla_fwd_ex(q, case.kv_pool, idx, case.sm_scale, case.kv_scale,
+                                   sinks=None if sinks is None else torch.from_numpy(sinks).to(DEV))
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(lse, lse2)
 
 
 # ---------------------------------------------------------------- pools past 4 GiB
