@@ -455,6 +455,39 @@ def test_pool_larger_than_4gib(H, D, kv, T, ctx):
     torch.cuda.empty_cache()
 
 
+
+def test_pool_larger_than_4gib_whole_lists():
+    """The same on the kernel for whole lists of 512-wide bf16 rows with two
+    workgroups per compute unit (each wave's entries ordered by slot range,
+    copies from 64-bit lane addresses)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    T, K = 2 * cus + 5, 256
+    ctx = 17 << 18                                      # 4,456,448 rows of 1 KiB: 4.56 GB
+    spec = synth.small_spec(T=T, H=16, Dqk=512, K=K, ctx=ctx, seed=29)
+    N, row_bytes = spec.N, 1024
+    assert N * row_bytes > 1 << 32
+    assert binding.sparse_mla_num_splits(T, 16, K, 512, 0, 0) == 1
+    print(f"pool past 4 GiB, whole lists: T{T} K{K} N={N}", flush=True)
+    case = synth.make_case(spec, device=DEV)
+    idx = case.topk_idx.cpu().numpy().copy()
+    first_high = (1 << 32) // row_bytes
+    rng = np.random.default_rng(29)
+    idx[0] = rng.choice(np.arange(first_high, N), size=K, replace=False)
+    idx[0, 7] = N - 1
+    idx[1, :8] = np.arange(first_high - 4, first_high + 4)
+    idx[2, :] = -1
+    idx[2, 100] = N - 1                                 # a list whose only row is the last one
+    idx_d = torch.from_numpy(idx).to(DEV)
+    out, lse = run(case, idx=idx_d)
+    ref_out, ref_lse = oracle_for_tokens(case, idx=idx_d)
+    compare(out, lse, ref_out, ref_lse, "bf16", f"pool {N * row_bytes / 2**30:.2f} GiB, whole lists")
+    row = case.kv_pool.reshape(N, 512)[N - 1].to(torch.bfloat16)
+    want = torch.where(row == 0, torch.zeros_like(row), row).expand(16, 512)
+    assert torch.equal(out[2].view(torch.int16), want.contiguous().view(torch.int16))
+    del case
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- attention sinks
 
 def _gpu_sinks(H, seed):
